@@ -1,0 +1,156 @@
+"""Pins for the oracle's dequantised GEMM, error bound and grouped GEMM (CPU only)."""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import codec, gemm, scaling
+from synth import bf16_bits_from_f32, moe_token_counts
+
+
+def _rand_codes(rng, shape, fmt):
+    """Random finite codes of the format (NaN / Inf codes excluded)."""
+    f = codec.FORMATS[fmt]
+    mag = rng.integers(0, f.max_code + 1, size=shape)
+    sign = rng.integers(0, 2, size=shape) << 7
+    return (mag | sign).astype(np.uint8)
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2")])
+def test_exact_dot_against_fractions(fa, fb):
+    rng = np.random.default_rng(1)
+    a = _rand_codes(rng, 300, fa)
+    b = _rand_codes(rng, 300, fb)
+    num, sh = gemm.exact_dot(a, fa, b, fb)
+    want = sum((Fraction(float(x)) * Fraction(float(y))
+                for x, y in zip(codec.decode(a, fa), codec.decode(b, fb))), Fraction(0))
+    assert Fraction(num, 2 ** sh) == want
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3")])
+def test_dequant_gemm_matches_exact_loops(fa, fb):
+    rng = np.random.default_rng(2)
+    qa = _rand_codes(rng, (6, 40), fa)
+    qb = _rand_codes(rng, (40, 5), fb)
+    sa, sb = np.float32(0.25), np.float32(3.0)
+    c = gemm.dequant_gemm(qa, fa, qb, fb, sa, sb)
+    ex = gemm.exact_gemm_small(qa, fa, qb, fb) * 0.75
+    assert np.array_equal(c, ex)
+
+
+def test_one_hot_and_permutation_select_columns():
+    rng = np.random.default_rng(3)
+    qa = _rand_codes(rng, (16, 32), "e4m3")
+    perm = rng.permutation(32)
+    qb = np.zeros((32, 32), dtype=np.uint8)
+    qb[perm, np.arange(32)] = 0x38                 # 1.0 in E4M3
+    c = gemm.dequant_gemm(qa, "e4m3", qb, "e4m3", np.float32(0.5), np.float32(1.0))
+    assert np.array_equal(c, codec.decode(qa, "e4m3")[:, perm] * 0.5)
+
+
+@pytest.mark.parametrize("K", [128, 4096, 16384])
+def test_all_max_operands_closed_form(K):
+    qa = np.full((2, K), 0x7E, dtype=np.uint8)
+    qb = np.full((K, 3), 0x7E, dtype=np.uint8)
+    c = gemm.dequant_gemm(qa, "e4m3", qb, "e4m3", np.float32(1), np.float32(1))
+    assert np.all(c == K * 448.0 ** 2)
+    qg = np.full((2, K), 0x7B, dtype=np.uint8)
+    c2 = gemm.dequant_gemm(qg, "e5m2", qb, "e4m3", np.float32(1), np.float32(1))
+    assert np.all(c2 == K * 448.0 * 57344.0)
+
+
+def test_zero_operand_gives_zero_and_zero_bound():
+    qa = np.zeros((4, 64), dtype=np.uint8)
+    qb = _rand_codes(np.random.default_rng(4), (64, 4), "e4m3")
+    assert not gemm.dequant_gemm(qa, "e4m3", qb, "e4m3", 1.0, 1.0).any()
+    assert not gemm.abs_bound(qa, "e4m3", qb, "e4m3", 1.0, 1.0).any()
+
+
+def test_abs_bound_is_relative_sum_of_magnitudes():
+    rng = np.random.default_rng(5)
+    qa = _rand_codes(rng, (3, 50), "e4m3")
+    qb = _rand_codes(rng, (50, 2), "e4m3")
+    b = gemm.abs_bound(qa, "e4m3", qb, "e4m3", np.float32(2), np.float32(0.5))
+    A, B = np.abs(codec.decode(qa, "e4m3")), np.abs(codec.decode(qb, "e4m3"))
+    for m in range(3):
+        for n in range(2):
+            assert np.isclose(b[m, n], 1e-5 * sum(A[m, k] * B[k, n] for k in range(50)), rtol=1e-12)
+
+
+def test_bf16_round_matches_synth_rounding_and_bracket():
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal(10000) * 100).astype(np.float32)
+    want = (bf16_bits_from_f32(x).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    assert np.array_equal(gemm.bf16_round(x.astype(np.float64)), want)
+    lo, hi = gemm.bf16_bracket(x.astype(np.float64), np.zeros_like(x, dtype=np.float64))
+    assert np.array_equal(lo, want) and np.array_equal(hi, want)
+    lo, hi = gemm.bf16_bracket(np.float64([1.0]), np.float64([2.0 ** -9]))
+    assert lo[0] == 1.0 == hi[0]                   # 1 - 2^-9 is a tie that rounds to even (1.0)
+    lo, hi = gemm.bf16_bracket(np.float64([1.0]), np.float64([2.0 ** -7]))
+    assert lo[0] == 1.0 - 2.0 ** -7 and hi[0] == 1.0 + 2.0 ** -7
+
+
+def test_grouped_reduces_to_per_group_gemm_with_uniform_scales():
+    rng = np.random.default_rng(7)
+    offs = np.array([0, 5, 5, 17])                 # includes an empty expert
+    K, N = 300, 260
+    qa = _rand_codes(rng, (17, K), "e4m3")
+    qb = _rand_codes(rng, (3, N, K), "e4m3")
+    sa = np.full((17, 3), np.float32(0.5), dtype=np.float32)
+    sb = np.full((3, 3, 3), np.float32(0.25), dtype=np.float32)
+    c = gemm.grouped_gemm(qa, sa, qb, sb, offs)
+    for g in range(3):
+        r0, r1 = offs[g], offs[g + 1]
+        want = gemm.dequant_gemm(qa[r0:r1], "e4m3", qb[g].T, "e4m3", 0.5, 0.25)
+        assert np.allclose(c[r0:r1], want, rtol=1e-13, atol=0)
+
+
+def test_grouped_matches_explicit_block_loops():
+    rng = np.random.default_rng(8)
+    offs = np.array([0, 3, 7])
+    K, N = 140, 129
+    qa = _rand_codes(rng, (7, K), "e4m3")
+    qb = _rand_codes(rng, (2, N, K), "e4m3")
+    sa = (2.0 ** rng.integers(-8, 8, size=(7, 2))).astype(np.float32)
+    sb = (2.0 ** rng.integers(-8, 8, size=(2, 2, 2))).astype(np.float32)
+    c = gemm.grouped_gemm(qa, sa, qb, sb, offs)
+    A = codec.decode(qa, "e4m3")
+    for m in range(7):
+        g = 0 if m < 3 else 1
+        for n in range(N):
+            tot = Fraction(0)
+            for k in range(K):
+                tot += Fraction(float(A[m, k])) * Fraction(float(codec.decode(qb[g, n, k], "e4m3"))) \
+                    * Fraction(float(sa[m, k // 128])) * Fraction(float(sb[g, n // 128, k // 128]))
+            assert c[m, n] == float(tot) or abs(c[m, n] - float(tot)) <= 1e-12 * abs(float(tot))
+
+
+def test_grouped_row_subset_matches_full():
+    rng = np.random.default_rng(9)
+    offs = np.array([0, 4, 9])
+    qa = _rand_codes(rng, (9, 256), "e4m3")
+    qb = _rand_codes(rng, (2, 128, 256), "e4m3")
+    sa = rng.uniform(0.1, 2, size=(9, 2)).astype(np.float32)
+    sb = rng.uniform(0.1, 2, size=(2, 1, 2)).astype(np.float32)
+    full = gemm.grouped_gemm(qa, sa, qb, sb, offs)
+    rows = np.array([8, 0, 4])
+    assert np.array_equal(gemm.grouped_gemm(qa, sa, qb, sb, offs, rows=rows), full[rows])
+
+
+def test_blockwise_quantize_then_grouped_approximates_float_product():
+    """End-to-end sanity: per-block FP8 GEMM is close to the fp64 product of the inputs."""
+    rng = np.random.default_rng(10)
+    A = rng.standard_normal((64, 256)).astype(np.float32)
+    W = (rng.standard_normal((128, 256)) * 0.02).astype(np.float32)
+    qa, sa = scaling.quantize_blockwise(A, 1, 128)
+    qw, sw = scaling.quantize_blockwise(W, 128, 128)
+    c = gemm.grouped_gemm(qa, sa, qw[None], sw[None], np.array([0, 64]))
+    ref = A.astype(np.float64) @ W.astype(np.float64).T
+    assert np.max(np.abs(c - ref)) < 0.05 * np.max(np.abs(ref))
+
+
+def test_moe_counts_recipe():
+    c = moe_token_counts()
+    assert c.sum() == 16384 and c.size == 8
+    assert np.all(c % 128 == 0) and c.min() >= 128 and c.max() <= 4096
