@@ -1,0 +1,358 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-tensor-scaled FP8 path on one MI355X.
+
+One step = the whole hot path on the FC1 forward layer of the Transformer
+Engine chapter's example (hidden 4096, ffn 16384; tokens = 4 x 2048):
+  1. fused amax + delayed-scaled E4M3 cast of X [8192 x 4096] bf16,
+  2. fused amax + delayed-scaled E4M3 cast-transpose of W [4096 x 16384] bf16,
+  3. FP8 GEMM  C[8192 x 16384] = X_q · W_qᵀ with fp32 accumulation and the
+     ×1/(s_x·s_w) epilogue, bf16 output,
+  4. the amax-history update of both tensors (next step's scales).
+Inputs are synthetic (seeded), resident in HBM before timing starts.
+
+Printed on stdout: ONE JSON line.  `value` is GEMM FLOP / step time (TFLOP/s
+of the whole step); `roofline` is the GEMM kernel alone (HIP events around
+each launch on its stream); `extra` holds the delayed-scaling stream
+(32 x 8192x4096, HBM GB/s of the fused amax+cast), the HYBRID dgrad GEMM and
+the fine-grained MoE grouped GEMM; `cpu_baseline` times the CPU oracle on a
+bounded slice of the same step.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 GEMM TFLOPS (% MFMA peak) at 8192x4096x16384; cast+amax HBM GB/s"
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--quick", action="store_true", help="headline step only (no extras, no CPU baseline)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--stream-dtype", default="bf16", choices=["bf16", "f32"])
+    return p.parse_args()
+
+
+class EventTimer:
+    """Pairs of HIP events recorded on the current stream around a launch."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __enter__(self):
+        s = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        self._s = s
+        return self
+
+    def __exit__(self, *exc):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((self._s, e))
+
+    def ms(self):
+        return [s.elapsed_time(e) for s, e in self.pairs]
+
+
+def headline(torch, fm, args):
+    from synth import fc1_forward
+
+    dev = torch.device("cuda:0")
+    M, K, N = 8192, 4096, 16384
+    log("generating FC1 inputs (X 8192x4096, W 4096x16384, 4 priors each) ...")
+    d = fc1_forward(M, K, N)
+    to_dev = lambda h: torch.from_numpy(h.data.view("int16")).to(dev).view(torch.bfloat16)  # noqa: E731
+    stX = fm.DelayedScalingState("e4m3", 16, device=dev)
+    stW = fm.DelayedScalingState("e4m3", 16, device=dev)
+    for pX, pW in zip(d["X_priors"], d["W_priors"]):
+        stX.quantize(to_dev(pX))
+        stX.update()
+        stW.quantize(to_dev(pW))
+        stW.update()
+    X, W = to_dev(d["X"]), to_dev(d["W"])
+    del d
+    qx = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    qwT = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    t_cx, t_cw, t_gemm = EventTimer(torch), EventTimer(torch), EventTimer(torch)
+
+    def step(timed):
+        if timed:
+            with t_cx:
+                stX.quantize(X, q=qx)
+            with t_cw:
+                stW.quantize(W, q_t=qwT)
+            with t_gemm:
+                fm.fp8_gemm(qx, "e4m3", qwT, "e4m3", stX.scale_inv, stW.scale_inv, c)
+        else:
+            stX.quantize(X, q=qx)
+            stW.quantize(W, q_t=qwT)
+            fm.fp8_gemm(qx, "e4m3", qwT, "e4m3", stX.scale_inv, stW.scale_inv, c)
+        stX.update()
+        stW.update()
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        step(True)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    flops = 2.0 * M * N * K
+    gemm_ms = statistics.mean(t_gemm.ms())
+    cx_ms, cw_ms = statistics.mean(t_cx.ms()), statistics.mean(t_cw.ms())
+    log(f"step {total_ms / args.steps:.3f} ms; gemm {gemm_ms * 1e3:.1f} us ({flops / gemm_ms / 1e9:.0f} TFLOP/s); "
+        f"cast X {cx_ms * 1e3:.1f} us; cast-transpose W {cw_ms * 1e3:.1f} us")
+    out = {
+        "ms_per_step": total_ms / args.steps,
+        "value": flops / (total_ms / args.steps) / 1e9,
+        "gemm_ms": gemm_ms,
+        "gemm_ms_median": statistics.median(t_gemm.ms()),
+        "gemm_tflops": flops / gemm_ms / 1e9,
+        "cast_x_us": cx_ms * 1e3,
+        "cast_x_gbs": M * K * 3 / (cx_ms * 1e-3) / 1e9,
+        "cast_transpose_w_us": cw_ms * 1e3,
+        "cast_transpose_w_gbs": K * N * 3 / (cw_ms * 1e-3) / 1e9,
+        "scale_x": stX.scale.item(),
+        "scale_w": stW.scale.item(),
+    }
+    del X, W, qx, qwT, c
+    torch.cuda.empty_cache()
+    return out
+
+
+def stream_bench(torch, fm, dtype, passes=3):
+    """Delayed-scaling stream: 32 distinct 8192x4096 tensors resident in HBM
+    (2 GiB bf16 / 4 GiB fp32, beyond the 256 MB last-level cache)."""
+    from synth import stream_step
+    import concurrent.futures as cf
+
+    dev = torch.device("cuda:0")
+    R, C = 8192, 4096
+    log(f"generating the 32-step stream ({dtype}) ...")
+    with cf.ThreadPoolExecutor(4) as ex:
+        hs = list(ex.map(lambda t: stream_step(t, R, C, dtype), range(32)))
+    xs = []
+    for h in hs:
+        arr = torch.from_numpy(h.data.view("int16") if dtype == "bf16" else h.data).to(dev)
+        xs.append(arr.view(torch.bfloat16) if dtype == "bf16" else arr)
+    del hs
+    q = torch.empty((R, C), dtype=torch.uint8, device=dev)
+    # reporting pass: per-step scale and saturation count
+    st = fm.DelayedScalingState("e4m3", 16, device=dev)
+    per_step = []
+    for t, x in enumerate(xs):
+        scale_used = st.scale.item()
+        st.quantize(x, q=q, count_saturation=True)
+        st.update()
+        per_step.append({"t": t, "scale": scale_used, "amax": st.amax.item(), "saturated": int(st.sat.item())})
+    # timing passes
+    timer = EventTimer(torch)
+    for _ in range(passes):
+        st = fm.DelayedScalingState("e4m3", 16, device=dev)
+        for x in xs:
+            with timer:
+                st.quantize(x, q=q, count_saturation=True)
+            st.update()
+    torch.cuda.synchronize()
+    ms = timer.ms()[32:] if passes > 1 else timer.ms()      # first pass warms up
+    bytes_per_step = R * C * ((2 if dtype == "bf16" else 4) + 1)
+    avg = statistics.mean(ms)
+    log(f"stream {dtype}: fused amax+cast {avg * 1e3:.1f} us/step = {bytes_per_step / (avg * 1e-3) / 1e9:.0f} GB/s")
+    del xs, q
+    torch.cuda.empty_cache()
+    return {"dtype": dtype, "us_per_step": avg * 1e3, "gbs": bytes_per_step / (avg * 1e-3) / 1e9,
+            "frac_hbm_peak": bytes_per_step / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "algorithmic_bytes_per_step": bytes_per_step, "per_step": per_step}
+
+
+def dgrad_bench(torch, fm, iters=20):
+    from synth import dgrad_hybrid
+
+    dev = torch.device("cuda:0")
+    M, K, N = 8192, 16384, 4096
+    log("generating dgrad inputs ...")
+    d = dgrad_hybrid(M, K, N, priors=False)
+    G = torch.from_numpy(d["dY"].data.view("int16")).to(dev).view(torch.bfloat16)
+    W = torch.from_numpy(d["W"].data.view("int16")).to(dev).view(torch.bfloat16)
+    del d
+    stG = fm.DelayedScalingState("e5m2", 16, device=dev)
+    stW = fm.DelayedScalingState("e4m3", 16, device=dev)
+    qg = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    qwT = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    for _ in range(2):                    # second pass casts with the amax-derived scale
+        stG.quantize(G, q=qg)
+        stG.update()
+        stW.quantize(W, q_t=qwT)
+        stW.update()
+    c = torch.empty((M, N), dtype=torch.float32, device=dev)
+    timer = EventTimer(torch)
+    for i in range(iters + 3):
+        if i < 3:
+            fm.fp8_gemm(qg, "e5m2", qwT, "e4m3", stG.scale_inv, stW.scale_inv, c)
+        else:
+            with timer:
+                fm.fp8_gemm(qg, "e5m2", qwT, "e4m3", stG.scale_inv, stW.scale_inv, c)
+    torch.cuda.synchronize()
+    ms = statistics.mean(timer.ms())
+    flops = 2.0 * M * N * K
+    log(f"dgrad E5M2xE4M3 -> fp32: {ms * 1e3:.1f} us = {flops / ms / 1e9:.0f} TFLOP/s")
+    del G, W, qg, qwT, c
+    torch.cuda.empty_cache()
+    return {"us": ms * 1e3, "tflops": flops / ms / 1e9, "frac_peak": flops / ms / 1e9 / PEAK_FP8_TFLOPS}
+
+
+def moe_bench(torch, fm, iters=20):
+    from synth import moe_grouped
+
+    dev = torch.device("cuda:0")
+    log("generating MoE inputs ...")
+    d = moe_grouped()
+    G, N, K = d["B"].shape
+    total = int(d["m_offsets"][-1])
+    A = torch.from_numpy(d["A"].data.view("int16")).to(dev).view(torch.bfloat16)
+    B = torch.from_numpy(d["B"].data.reshape(G * N, K).view("int16")).to(dev).view(torch.bfloat16)
+    offs = torch.from_numpy(d["m_offsets"].astype("int32")).to(dev)
+    counts = d["counts"].tolist()
+    del d
+    qa = torch.empty((total, K), dtype=torch.uint8, device=dev)
+    sa = torch.empty((total, K // 128), dtype=torch.float32, device=dev)
+    qb = torch.empty((G * N, K), dtype=torch.uint8, device=dev)
+    sb = torch.empty((G * N // 128, K // 128), dtype=torch.float32, device=dev)
+    c = torch.empty((total, N), dtype=torch.bfloat16, device=dev)
+    ta, tb, tg = EventTimer(torch), EventTimer(torch), EventTimer(torch)
+    for i in range(iters + 3):
+        if i < 3:
+            fm.fp8_quantize_blockwise(A, 1, "e4m3", qa, sa)
+            fm.fp8_quantize_blockwise(B, 128, "e4m3", qb, sb)
+            fm.fp8_grouped_gemm(qa, sa, qb.view(G, N, K), sb.view(G, N // 128, K // 128), offs, c)
+            continue
+        with ta:
+            fm.fp8_quantize_blockwise(A, 1, "e4m3", qa, sa)
+        with tb:
+            fm.fp8_quantize_blockwise(B, 128, "e4m3", qb, sb)
+        with tg:
+            fm.fp8_grouped_gemm(qa, sa, qb.view(G, N, K), sb.view(G, N // 128, K // 128), offs, c)
+    torch.cuda.synchronize()
+    g_ms = statistics.mean(tg.ms())
+    flops = 2.0 * total * N * K
+    a_ms, b_ms = statistics.mean(ta.ms()), statistics.mean(tb.ms())
+    log(f"moe grouped: gemm {g_ms * 1e3:.1f} us = {flops / g_ms / 1e9:.0f} TFLOP/s; "
+        f"blockwise A {a_ms * 1e3:.1f} us, W {b_ms * 1e3:.1f} us")
+    del A, B, qa, sa, qb, sb, c
+    torch.cuda.empty_cache()
+    return {"token_counts": counts, "gemm_us": g_ms * 1e3, "gemm_tflops": flops / g_ms / 1e9,
+            "frac_peak": flops / g_ms / 1e9 / PEAK_FP8_TFLOPS, "blockwise_a_us": a_ms * 1e3,
+            "blockwise_w_us": b_ms * 1e3,
+            "blockwise_a_gbs": total * K * 3 / (a_ms * 1e-3) / 1e9,
+            "blockwise_w_gbs": G * N * K * 3 / (b_ms * 1e-3) / 1e9}
+
+
+def cpu_baseline(rows=512):
+    """The CPU oracle on a bounded slice of the headline step: delayed-scaled cast
+    of `rows` rows of X, cast of the whole W, and the dequantised GEMM of those
+    rows (fp64 BLAS).  Reported in TFLOP/s of the GEMM FLOPs of the slice."""
+    import numpy as np
+
+    from oracle import gemm, scaling
+    from synth import fc1_forward
+
+    d = fc1_forward(8192, 4096, 16384, priors=False)
+    x = scaling.widen(d["X"].data[:rows], "bf16")
+    w = scaling.widen(d["W"].data, "bf16")
+    threads = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        blas = threads
+    t0 = time.perf_counter()
+    sx = scaling.DelayedScaling("e4m3", 16)
+    sw = scaling.DelayedScaling("e4m3", 16)
+    qx, ax, _ = scaling.quantize(x, sx.scale, "e4m3")
+    qw, aw, _ = scaling.quantize(w, sw.scale, "e4m3")
+    c = gemm.dequant_gemm(qx, "e4m3", qw, "e4m3", sx.scale_inv, sw.scale_inv)
+    sx.update(ax)
+    sw.update(aw)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * 16384 * 4096
+    assert np.isfinite(c).all()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"oracle (numpy) on {rows} of 8192 rows: amax+cast of X[{rows}x4096] and of all of "
+                      f"W[4096x16384] (1 thread), fp64 dequantised GEMM {rows}x4096x16384 "
+                      f"(BLAS, {blas} threads of {threads} available); {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the path is single-GPU; see the design notes for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import fp8_precision_numerics_amd as fm
+
+    fm.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    head = headline(torch, fm, args)
+    extra = {"headline": head}
+    if not args.quick:
+        extra["stream"] = stream_bench(torch, fm, args.stream_dtype)
+        extra["dgrad"] = dgrad_bench(torch, fm)
+        extra["moe_grouped"] = moe_bench(torch, fm)
+    cpu = None
+    if not args.quick and not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline()
+    line = {
+        "metric": METRIC,
+        "value": round(head["value"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": "fc1_forward_delayed_scaling", "M": 8192, "K": 4096, "N": 16384,
+                   "inputs": "bf16 X (N(0,1), 0.1% x100 outliers), bf16 W N(0,0.02)", "fp8": "e4m3 x e4m3",
+                   "out": "bf16", "history_len": 16, "amax_rule": "max"},
+        "roofline": {"bound": "mfma", "achieved": round(head["gemm_tflops"], 1), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(head["gemm_tflops"] / PEAK_FP8_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,230 @@
+"""ctypes binding of libfp8mi (include/fp8mi.h): argument marshalling only.
+
+Every function here takes torch tensors that already live on the GPU, turns
+them into raw device pointers, sizes and enum codes, and calls the C entry
+point of the same name on the current HIP stream (or the stream given).  No
+arithmetic of the FP8 path happens in Python: amax, scaling, casting and the
+GEMMs all run in the HIP kernels of libfp8mi.so.  If the library is missing
+or cannot be loaded, every call raises; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["E4M3", "E5M2", "F32", "BF16", "Fp8Error", "load_library", "library_path",
+           "status_string", "version", "fp8_quantize", "fp8_amax_update", "fp8_gemm",
+           "fp8_quantize_blockwise", "fp8_grouped_gemm", "EXPORTED_SYMBOLS"]
+
+E4M3, E5M2 = 0, 1
+F32, BF16 = 0, 1
+FORMATS = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
+
+EXPORTED_SYMBOLS = ("fp8mi_status_string", "fp8mi_version", "fp8_quantize", "fp8_amax_update",
+                    "fp8_gemm", "fp8_quantize_blockwise", "fp8_grouped_gemm")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def library_path() -> str:
+    return os.environ.get("FP8MI_LIBRARY", os.path.join(_HERE, "lib", "libfp8mi.so"))
+
+
+class Fp8Error(RuntimeError):
+    """A libfp8mi entry point returned a non-zero status."""
+
+    def __init__(self, func: str, status: int):
+        self.status = status
+        super().__init__(f"{func} failed: status {status} ({status_string(status)})")
+
+
+def load_library():
+    """Load libfp8mi.so once and declare the C signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libfp8mi.so is not built ({path} missing); run __graft_entry__.build() "
+                           "or python -m fp8_precision_numerics_amd.build")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.fp8mi_status_string.argtypes = [ctypes.c_int]
+    lib.fp8mi_status_string.restype = ctypes.c_char_p
+    lib.fp8mi_version.argtypes = []
+    lib.fp8mi_version.restype = ctypes.c_int
+    lib.fp8_quantize.argtypes = [vp, ctypes.c_int, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp]
+    lib.fp8_quantize.restype = ctypes.c_int
+    lib.fp8_amax_update.argtypes = [vp, i32, vp, vp, ctypes.c_int, vp, vp, vp, vp]
+    lib.fp8_amax_update.restype = ctypes.c_int
+    lib.fp8_gemm.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, ctypes.c_int, vp]
+    lib.fp8_gemm.restype = ctypes.c_int
+    lib.fp8_quantize_blockwise.argtypes = [vp, ctypes.c_int, i64, i64, i32, ctypes.c_int, vp, vp, vp]
+    lib.fp8_quantize_blockwise.restype = ctypes.c_int
+    lib.fp8_grouped_gemm.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, ctypes.c_int, vp]
+    lib.fp8_grouped_gemm.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().fp8mi_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(load_library().fp8mi_version())
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _xtype(x: torch.Tensor) -> int:
+    if x.dtype == torch.float32:
+        return F32
+    if x.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"input dtype must be float32 or bfloat16, got {x.dtype}")
+
+
+def _fmt(f) -> int:
+    try:
+        return FORMATS[f]
+    except KeyError:
+        raise ValueError(f"unknown FP8 format {f!r}") from None
+
+
+def _check(t, name, dtype=None, numel=None, device=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _rows_cols(x: torch.Tensor):
+    if x.dim() == 0:
+        return 1, 1
+    cols = x.shape[-1]
+    return (x.numel() // cols if cols else 0), cols
+
+
+def _call(name, status):
+    if status != 0:
+        raise Fp8Error(name, status)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def fp8_quantize(x, fmt, scale=None, q=None, q_t=None, amax=None, sat=None, stream=None) -> None:
+    """Fused amax + scaled saturating cast of x ([rows x cols], fp32 or bf16).
+
+    q: uint8 [rows x cols] or None; q_t: uint8 [cols x rows] or None;
+    scale: fp32[1] device scale; amax: fp32[1] (overwritten); sat: int64[1]
+    (overwritten with the saturated-element count).
+    """
+    lib = load_library()
+    _check(x, "x", (torch.float32, torch.bfloat16))
+    rows, cols = _rows_cols(x)
+    dev = x.device
+    _check(scale, "scale", torch.float32, 1, dev)
+    _check(q, "q", torch.uint8, rows * cols, dev)
+    _check(q_t, "q_t", torch.uint8, rows * cols, dev)
+    _check(amax, "amax", torch.float32, 1, dev)
+    _check(sat, "sat", torch.int64, 1, dev)
+    with torch.cuda.device(dev):
+        _call("fp8_quantize", lib.fp8_quantize(_p(x), _xtype(x), rows, cols, _fmt(fmt), _p(scale), _p(q),
+                                               _p(q_t), _p(amax), _p(sat), _stream(stream)))
+
+
+def fp8_amax_update(history, head, amax, fmt, scale, scale_inv, status=None, stream=None) -> None:
+    """Delayed-scaling step: push amax into the ring, recompute scale / scale_inv."""
+    lib = load_library()
+    dev = history.device
+    _check(history, "history", torch.float32, None, dev)
+    _check(head, "head", torch.int32, 1, dev)
+    _check(amax, "amax", torch.float32, 1, dev)
+    _check(scale, "scale", torch.float32, 1, dev)
+    _check(scale_inv, "scale_inv", torch.float32, 1, dev)
+    _check(status, "status", torch.int32, 1, dev)
+    with torch.cuda.device(dev):
+        _call("fp8_amax_update", lib.fp8_amax_update(_p(history), history.numel(), _p(head), _p(amax),
+                                                     _fmt(fmt), _p(scale), _p(scale_inv), _p(status),
+                                                     _stream(stream)))
+
+
+def fp8_gemm(a, fa, b, fb, sinv_a, sinv_b, c, stream=None) -> None:
+    """C[M x N] = (A[M x K] · B[N x K]ᵀ) · sinv_a · sinv_b with FP8 codes A, B."""
+    lib = load_library()
+    dev = a.device
+    _check(a, "a", torch.uint8, None, dev)
+    _check(b, "b", torch.uint8, None, dev)
+    _check(sinv_a, "sinv_a", torch.float32, 1, dev)
+    _check(sinv_b, "sinv_b", torch.float32, 1, dev)
+    _check(c, "c", (torch.float32, torch.bfloat16), None, dev)
+    M, K = a.shape
+    N, K2 = b.shape
+    if K2 != K or tuple(c.shape) != (M, N):
+        raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)}, c {tuple(c.shape)}")
+    ctype = F32 if c.dtype == torch.float32 else BF16
+    with torch.cuda.device(dev):
+        _call("fp8_gemm", lib.fp8_gemm(_p(a), _fmt(fa), _p(b), _fmt(fb), M, N, K, _p(sinv_a), _p(sinv_b),
+                                       _p(c), ctype, _stream(stream)))
+
+
+def fp8_quantize_blockwise(x, block_rows, fmt, q, scale_inv, stream=None) -> None:
+    """Per-block current scaling of x [rows x cols] with block_rows x 128 blocks."""
+    lib = load_library()
+    _check(x, "x", (torch.float32, torch.bfloat16))
+    rows, cols = _rows_cols(x)
+    dev = x.device
+    _check(q, "q", torch.uint8, rows * cols, dev)
+    nbr = (rows + block_rows - 1) // block_rows if block_rows > 0 else 0
+    _check(scale_inv, "scale_inv", torch.float32, nbr * ((cols + 127) // 128), dev)
+    with torch.cuda.device(dev):
+        _call("fp8_quantize_blockwise", lib.fp8_quantize_blockwise(_p(x), _xtype(x), rows, cols, int(block_rows),
+                                                                   _fmt(fmt), _p(q), _p(scale_inv),
+                                                                   _stream(stream)))
+
+
+def fp8_grouped_gemm(a, sinv_a, b, sinv_b, m_offsets, c, stream=None) -> None:
+    """Grouped fine-grained GEMM: a [total_m x K], b [G x N x K], m_offsets int32 [G+1]."""
+    lib = load_library()
+    dev = a.device
+    _check(a, "a", torch.uint8, None, dev)
+    _check(b, "b", torch.uint8, None, dev)
+    _check(sinv_a, "sinv_a", torch.float32, None, dev)
+    _check(sinv_b, "sinv_b", torch.float32, None, dev)
+    _check(m_offsets, "m_offsets", torch.int32, None, dev)
+    _check(c, "c", (torch.float32, torch.bfloat16), None, dev)
+    total_m, K = a.shape
+    G, N, K2 = b.shape
+    if K2 != K or tuple(c.shape) != (total_m, N) or m_offsets.numel() != G + 1:
+        raise ValueError("shape mismatch in fp8_grouped_gemm")
+    ctype = F32 if c.dtype == torch.float32 else BF16
+    with torch.cuda.device(dev):
+        _call("fp8_grouped_gemm", lib.fp8_grouped_gemm(_p(a), _p(sinv_a), _p(b), _p(sinv_b), _p(m_offsets), G,
+                                                       total_m, N, K, _p(c), ctype, _stream(stream)))

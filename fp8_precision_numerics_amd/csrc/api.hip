@@ -1,0 +1,153 @@
+// extern "C" entry points of libfp8mi: argument validation, device check,
+// and dispatch to the kernel launchers.  The contract of each function
+// (arguments, layout, ownership, errors) is stated in include/fp8mi.h.
+#include <stdint.h>
+
+#include <atomic>
+
+#include "fp8mi.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = 0x7FFFFFFF;             // kernels index rows/cols with 32-bit ints
+constexpr int64_t kMaxElems = (int64_t)1 << 40;     // sanity bound on any one tensor
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];         // 0 unknown, 1 gfx950, -1 not usable
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool fmt_ok(int f) { return f == FP8MI_E4M3 || f == FP8MI_E5M2; }
+bool dtype_ok(int d) { return d == FP8MI_F32 || d == FP8MI_BF16; }
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8MI_ERR_DEVICE;
+  int state = g_device_ok[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    state = -1;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+      const char* a = prop.gcnArchName;
+      if (a[0] == 'g' && a[1] == 'f' && a[2] == 'x' && a[3] == '9' && a[4] == '5' && a[5] == '0')
+        state = 1;
+    }
+    g_device_ok[dev].store(state, std::memory_order_relaxed);
+  }
+  return state == 1 ? FP8MI_OK : FP8MI_ERR_DEVICE;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? FP8MI_OK : FP8MI_ERR_LAUNCH; }
+
+bool dims_ok(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0 || rows > kMaxElems || cols > kMaxElems) return false;
+  if (rows != 0 && cols > kMaxElems / rows) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8mi_status_string(int status) {
+  switch (status) {
+    case FP8MI_OK: return "ok";
+    case FP8MI_ERR_NULL: return "a required pointer is NULL";
+    case FP8MI_ERR_SHAPE: return "invalid or inconsistent size";
+    case FP8MI_ERR_ALIGN: return "pointer or size breaks the alignment rule";
+    case FP8MI_ERR_FORMAT: return "unknown FP8 format";
+    case FP8MI_ERR_DTYPE: return "unknown data type";
+    case FP8MI_ERR_LAUNCH: return "kernel launch failed";
+    case FP8MI_ERR_DEVICE: return "no usable gfx950 device is current";
+    default: return "unknown status";
+  }
+}
+
+int fp8mi_version(void) { return 100; }
+
+int fp8_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, const float* scale,
+                 uint8_t* q, uint8_t* q_t, float* amax, unsigned long long* sat, void* stream) {
+  if (!dtype_ok(xtype)) return FP8MI_ERR_DTYPE;
+  if (!fmt_ok(fmt)) return FP8MI_ERR_FORMAT;
+  if (!dims_ok(rows, cols)) return FP8MI_ERR_SHAPE;
+  const int64_t n = rows * cols;
+  if (!q && !q_t && !amax) return FP8MI_ERR_NULL;
+  if ((q || q_t || sat) && !scale) return FP8MI_ERR_NULL;
+  if (n > 0 && !x) return FP8MI_ERR_NULL;
+  if ((x && !aligned16(x)) || (q && !aligned16(q)) || (q_t && !aligned16(q_t))) return FP8MI_ERR_ALIGN;
+  if (q_t && ((rows & 15) || (cols & 15))) return FP8MI_ERR_ALIGN;
+  if (q_t && (rows + 127) / 128 > 65535) return FP8MI_ERR_SHAPE;
+  if ((cols + 127) / 128 > kMaxDim) return FP8MI_ERR_SHAPE;
+  if (!amax && !sat && n == 0) return FP8MI_OK;
+  const int dev = check_device();
+  if (dev != FP8MI_OK) return dev;
+  return launched(fp8mi::launch_quantize(x, xtype, rows, cols, fmt, scale, q, q_t, amax, sat,
+                                         (hipStream_t)stream));
+}
+
+int fp8_amax_update(float* history, int32_t history_len, int32_t* head, const float* amax, int fmt,
+                    float* scale, float* scale_inv, int32_t* status, void* stream) {
+  if (!fmt_ok(fmt)) return FP8MI_ERR_FORMAT;
+  if (!history || !head || !amax || !scale || !scale_inv) return FP8MI_ERR_NULL;
+  if (history_len < 1 || history_len > 4096) return FP8MI_ERR_SHAPE;
+  const int dev = check_device();
+  if (dev != FP8MI_OK) return dev;
+  return launched(fp8mi::launch_amax_update(history, history_len, head, amax, fmt, scale, scale_inv,
+                                            status, (hipStream_t)stream));
+}
+
+int fp8_gemm(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t M, int64_t N, int64_t K,
+             const float* sinv_a, const float* sinv_b, void* C, int ctype, void* stream) {
+  if (!fmt_ok(fa) || !fmt_ok(fb)) return FP8MI_ERR_FORMAT;
+  if (!dtype_ok(ctype)) return FP8MI_ERR_DTYPE;
+  if (M < 0 || N < 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8MI_ERR_SHAPE;
+  if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N)) return FP8MI_ERR_SHAPE;
+  if ((K & 15) != 0) return FP8MI_ERR_ALIGN;
+  if (((M + 127) / 128) * ((N + 127) / 128) > kMaxDim) return FP8MI_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8MI_OK;
+  if (!A || !B || !sinv_a || !sinv_b || !C) return FP8MI_ERR_NULL;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return FP8MI_ERR_ALIGN;
+  const int dev = check_device();
+  if (dev != FP8MI_OK) return dev;
+  return launched(fp8mi::launch_gemm(A, fa, B, fb, M, N, K, sinv_a, sinv_b, C, ctype,
+                                     (hipStream_t)stream));
+}
+
+int fp8_quantize_blockwise(const void* x, int xtype, int64_t rows, int64_t cols, int32_t block_rows,
+                           int fmt, uint8_t* q, float* scale_inv, void* stream) {
+  if (!dtype_ok(xtype)) return FP8MI_ERR_DTYPE;
+  if (!fmt_ok(fmt)) return FP8MI_ERR_FORMAT;
+  if (block_rows != 1 && block_rows != 128) return FP8MI_ERR_SHAPE;
+  if (!dims_ok(rows, cols)) return FP8MI_ERR_SHAPE;
+  if ((cols & 15) != 0) return FP8MI_ERR_ALIGN;
+  if (block_rows == 128 && ((rows + 127) / 128 > 65535 || (cols + 127) / 128 > kMaxDim))
+    return FP8MI_ERR_SHAPE;
+  if (rows * cols == 0) return FP8MI_OK;
+  if (!x || !q || !scale_inv) return FP8MI_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q)) return FP8MI_ERR_ALIGN;
+  const int dev = check_device();
+  if (dev != FP8MI_OK) return dev;
+  return launched(fp8mi::launch_quantize_blockwise(x, xtype, rows, cols, block_rows, fmt, q,
+                                                   scale_inv, (hipStream_t)stream));
+}
+
+int fp8_grouped_gemm(const uint8_t* A, const float* sinv_a, const uint8_t* B, const float* sinv_b,
+                     const int32_t* m_offsets, int32_t G, int64_t total_m, int64_t N, int64_t K,
+                     void* C, int ctype, void* stream) {
+  if (!dtype_ok(ctype)) return FP8MI_ERR_DTYPE;
+  if (G < 1 || G > 1024) return FP8MI_ERR_SHAPE;
+  if (total_m < 0 || N < 0 || K <= 0 || total_m > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return FP8MI_ERR_SHAPE;
+  if (!dims_ok(total_m, K) || !dims_ok(N, K) || !dims_ok((int64_t)G * N, K) || !dims_ok(total_m, N))
+    return FP8MI_ERR_SHAPE;
+  if ((K & 15) != 0) return FP8MI_ERR_ALIGN;
+  if (((total_m + 127) / 128 + G) * ((N + 127) / 128) > kMaxDim) return FP8MI_ERR_SHAPE;
+  if (total_m == 0 || N == 0) return FP8MI_OK;
+  if (!A || !sinv_a || !B || !sinv_b || !m_offsets || !C) return FP8MI_ERR_NULL;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return FP8MI_ERR_ALIGN;
+  const int dev = check_device();
+  if (dev != FP8MI_OK) return dev;
+  return launched(fp8mi::launch_grouped_gemm(A, sinv_a, B, sinv_b, m_offsets, G, total_m, N, K, C,
+                                             ctype, (hipStream_t)stream));
+}
+
+}  // extern "C"

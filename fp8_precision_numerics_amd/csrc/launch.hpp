@@ -1,0 +1,32 @@
+// Internal launchers behind the C ABI (include/fp8mi.h).  Arguments are
+// already validated by api.hip; each launcher only enqueues kernels on the
+// given stream and returns the HIP launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8mi {
+
+hipError_t launch_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt,
+                           const float* scale, uint8_t* q, uint8_t* q_t, float* amax,
+                           unsigned long long* sat, hipStream_t stream);
+
+hipError_t launch_quantize_blockwise(const void* x, int xtype, int64_t rows, int64_t cols,
+                                     int block_rows, int fmt, uint8_t* q, float* scale_inv,
+                                     hipStream_t stream);
+
+hipError_t launch_amax_update(float* history, int history_len, int32_t* head, const float* amax,
+                              int fmt, float* scale, float* scale_inv, int32_t* status,
+                              hipStream_t stream);
+
+hipError_t launch_gemm(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t M, int64_t N,
+                       int64_t K, const float* sinv_a, const float* sinv_b, void* C, int ctype,
+                       hipStream_t stream);
+
+hipError_t launch_grouped_gemm(const uint8_t* A, const float* sinv_a, const uint8_t* B,
+                               const float* sinv_b, const int32_t* m_offsets, int G,
+                               int64_t total_m, int64_t N, int64_t K, void* C, int ctype,
+                               hipStream_t stream);
+
+}  // namespace fp8mi

@@ -1,0 +1,189 @@
+/*
+ * fp8mi.h — per-tensor-scaled FP8 matrix multiply with delayed scaling,
+ * native to AMD Instinct MI355X (gfx950, CDNA4).  C ABI.
+ *
+ * The operations follow these pages:
+ *   [TE]  "4.2 Hopper I — Transformer Engine·FP8" (aegloslab.com), §4.2.3–§4.2.6,
+ *         §4.2.8 (formats, amax-based per-tensor scale, delayed scaling from an
+ *         amax history, FP8 GEMM with FP32 accumulation and x(1/scale) restore,
+ *         the HYBRID recipe with history length 16 and the "max" rule, OCP FP8).
+ *   [FMT] "FP8 and low-precision formats" (aiunderstanding.org), "Deep dive" and
+ *         "Technical insight" (E4M3/E5M2 bit splits, per-tensor or per-block
+ *         scale factors, high-precision partial sums).
+ *   [DG]  "#fp8" tag page (discuss.pytorch.kr), DeepGEMM entry (MoE grouped
+ *         GEMM, two-level "promotion" of FP8 partial sums).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named as device pointers must point to memory of the GPU that is
+ *   current on the calling thread; all scalars (sizes, formats, flags) are host
+ *   values.  Passing host memory where device memory is required is undefined.
+ * - The caller allocates and owns every buffer.  No entry point allocates,
+ *   frees or keeps device memory.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is
+ *   asynchronous: results are valid after the caller synchronises the stream.
+ *   Nothing synchronises the host.
+ * - Argument errors are detected on the host before anything is launched and
+ *   returned as a negative fp8mi_status; nothing is enqueued in that case.
+ *   A failed launch returns FP8MI_ERR_LAUNCH.  Device faults surface at the
+ *   caller's next synchronisation.  Numeric anomalies (NaN/Inf/zero amax) are
+ *   not errors: see fp8_amax_update.  Nothing is thrown across the ABI.
+ * - FP8 data is uint8 codes in the OCP 8-bit floating-point formats:
+ *   E4M3 (bias 7, no Inf, NaN = S.1111.111, max 448) and E5M2 (bias 15,
+ *   IEEE-like Inf/NaN, max 57344).
+ * - Row-major everywhere; "[R x C]" means R rows of C contiguous elements.
+ */
+#ifndef FP8MI_H
+#define FP8MI_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define FP8MI_API __attribute__((visibility("default")))
+#else
+#define FP8MI_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FP8MI_E4M3 = 0, FP8MI_E5M2 = 1 } fp8mi_format;
+typedef enum { FP8MI_F32 = 0, FP8MI_BF16 = 1 } fp8mi_dtype;
+
+typedef enum {
+  FP8MI_OK = 0,
+  FP8MI_ERR_NULL = -1,    /* a required pointer is NULL                          */
+  FP8MI_ERR_SHAPE = -2,   /* a size is negative, too large or inconsistent       */
+  FP8MI_ERR_ALIGN = -3,   /* a pointer or leading size breaks the alignment rule */
+  FP8MI_ERR_FORMAT = -4,  /* unknown fp8mi_format                                */
+  FP8MI_ERR_DTYPE = -5,   /* unknown fp8mi_dtype                                 */
+  FP8MI_ERR_LAUNCH = -6,  /* the HIP runtime rejected a kernel launch            */
+  FP8MI_ERR_DEVICE = -7   /* no usable gfx950 device is current                  */
+} fp8mi_status;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+FP8MI_API const char* fp8mi_status_string(int status);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+FP8MI_API int fp8mi_version(void);
+
+/*
+ * fp8_quantize — fused amax reduction + scaled saturating cast ([TE] §4.2.4).
+ *
+ *   p      = fp32(x[i] * scale[0])                  (one fp32 multiply, RNE)
+ *   code   = round_to_fp8(p): nearest, ties to even mantissa; |p| > max and
+ *            +-Inf saturate to +-max; NaN -> sign|0x7F; sign always kept
+ *   amax   = max_i |x[i]| of the UNSCALED input, taken as the largest
+ *            (bits & 0x7FFFFFFF) — exact and order-free; NaN/Inf propagate
+ *   sat    = #{ i : |p| > max }  (Inf counts, NaN does not)
+ *
+ * One read of x produces every output ([TE] §4.2.4: delayed scaling exists so
+ * that the tensor is traversed once).
+ *
+ * x        device, [rows x cols] of xtype (fp32 or bf16 bit patterns); 16-B aligned.
+ * scale    device, 1 fp32: the scale to apply (normally the delayed scale kept
+ *          by fp8_amax_update).  May be NULL only when q and q_t are both NULL.
+ * q        device, [rows x cols] uint8 codes, or NULL; 16-B aligned.
+ * q_t      device, [cols x rows] uint8 codes of the transpose, or NULL
+ *          ("cast-transpose": the K-contiguous layout fp8_gemm wants for an
+ *          operand stored [K x N]).  When non-NULL, rows and cols must be
+ *          multiples of 16.
+ * amax     device, 1 fp32, overwritten (not accumulated), or NULL.
+ * sat      device, 1 uint64, overwritten, or NULL.
+ * At least one of q, q_t, amax must be non-NULL.  rows*cols may be 0 (then
+ * amax = 0 and sat = 0).
+ */
+FP8MI_API int fp8_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt,
+                 const float* scale, uint8_t* q, uint8_t* q_t, float* amax,
+                 unsigned long long* sat, void* stream);
+
+/*
+ * fp8_amax_update — delayed-scaling history step ([TE] §4.2.4 "delayed
+ * scaling", §4.2.6 recipe: amax_history_len, amax_compute_algo = "max").
+ *
+ *   h = *head;  history[h] = *amax;  *head = (h + 1) % history_len;
+ *   m = max(history[0 .. history_len-1])   (over fp32 bit patterns, so NaN > Inf)
+ *   if (0 < m < Inf and s = fp32(MAX / m) is finite):
+ *        *scale = s;  *scale_inv = fp32(1 / s)      (both correctly rounded)
+ *   else: *scale and *scale_inv are left unchanged and bit 0 of *status is set.
+ *
+ * MAX is 448 for E4M3 and 57344 for E5M2.  The new scale is the one the NEXT
+ * fp8_quantize of this tensor should use: the amax of the step just cast
+ * never influences its own cast.
+ *
+ * history    device, history_len fp32 (caller-owned; zero it for a fresh tensor).
+ * head       device, 1 int32 in [0, history_len).  An out-of-range value is
+ *            treated as 0 and bit 1 of *status is set.
+ * amax       device, 1 fp32 (e.g. fp8_quantize's amax output).
+ * scale, scale_inv  device, 1 fp32 each (fresh tensor: 1.0 and 1.0).
+ * status     device, 1 int32 of sticky flags, or NULL.
+ * history_len in [1, 4096].
+ */
+FP8MI_API int fp8_amax_update(float* history, int32_t history_len, int32_t* head, const float* amax,
+                    int fmt, float* scale, float* scale_inv, int32_t* status, void* stream);
+
+/*
+ * fp8_gemm — FP8 x FP8 GEMM with FP32 accumulation and the x(1/scale) restore
+ * in the epilogue ([TE] §4.2.4; [FMT] "Technical insight").
+ *
+ *   C[m][n] = ( sum_k dec_fa(A[m][k]) * dec_fb(B[n][k]) ) * sinv_a[0] * sinv_b[0]
+ *
+ * A       device, [M x K] uint8 codes of format fa (K contiguous), 16-B aligned.
+ * B       device, [N x K] uint8 codes of format fb (K contiguous: the transpose
+ *         of the logical K x N operand, as fp8_quantize's q_t writes it), 16-B aligned.
+ * sinv_a, sinv_b  device, 1 fp32 each: the inverse scales of A and B.
+ * C       device, [M x N] of ctype (fp32, or bf16 rounded to nearest even),
+ *         16-B aligned.
+ * K must be a multiple of 16 (and > 0); M, N >= 0 (M or N == 0 is a no-op).
+ * Accumulation is fp32 in the matrix cores; the order of the sum is not fixed.
+ */
+FP8MI_API int fp8_gemm(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t M, int64_t N, int64_t K,
+             const float* sinv_a, const float* sinv_b, void* C, int ctype, void* stream);
+
+/*
+ * fp8_quantize_blockwise — current (not delayed) per-block scaling
+ * ([FMT] "Deep dive": per-tensor or per-block scale factors; [DG]).
+ *
+ * Blocks are block_rows x 128 (block_rows = 1 for activations, 128 for
+ * weights).  For every block b:  m_b = max |x| over the block (bit patterns);
+ *   s_b = fp32(MAX / m_b) if 0 < m_b < Inf and the quotient is finite, else 1;
+ *   q   = round_to_fp8(fp32(x * s_b))  (as fp8_quantize);
+ *   scale_inv[b] = fp32(1 / s_b).
+ *
+ * x          device, [rows x cols] of xtype, 16-B aligned.
+ * q          device, [rows x cols] uint8, 16-B aligned.
+ * scale_inv  device, [ceil(rows/block_rows) x ceil(cols/128)] fp32.
+ * cols must be a multiple of 16; block_rows is 1 or 128.
+ */
+FP8MI_API int fp8_quantize_blockwise(const void* x, int xtype, int64_t rows, int64_t cols, int32_t block_rows,
+                           int fmt, uint8_t* q, float* scale_inv, void* stream);
+
+/*
+ * fp8_grouped_gemm — fine-grained-scaled grouped GEMM for MoE experts with
+ * two-level accumulation ([DG]: grouped GEMM, "promotion" of FP8 partial sums).
+ *
+ * Expert g owns rows [m_offsets[g], m_offsets[g+1]) of A and C.  For each row
+ * m of expert g and each 128-wide K block kb:
+ *   P = sum_{k in kb} dec(A[m][k]) * dec(B[g][n][k])   (an FP32 MFMA partial)
+ *   C[m][n] += sinv_a[m][kb] * sinv_b[g][n/128][kb] * P  (FP32 "promotion")
+ *
+ * A          device, [total_m x K] E4M3 codes.
+ * sinv_a     device, [total_m x ceil(K/128)] fp32 (per 1x128 tile).
+ * B          device, [G x N x K] E4M3 codes (each expert's weight, K contiguous).
+ * sinv_b     device, [G x ceil(N/128) x ceil(K/128)] fp32 (per 128x128 block).
+ * m_offsets  device, G+1 int32, non-decreasing, m_offsets[0] = 0,
+ *            m_offsets[G] = total_m.  Offsets that break this are clamped to
+ *            [0, total_m] (rows outside every expert are left untouched).
+ * C          device, [total_m x N] of ctype.
+ * K must be a multiple of 16; G in [1, 1024]; all pointers 16-B aligned.
+ */
+FP8MI_API int fp8_grouped_gemm(const uint8_t* A, const float* sinv_a, const uint8_t* B, const float* sinv_b,
+                     const int32_t* m_offsets, int32_t G, int64_t total_m, int64_t N, int64_t K,
+                     void* C, int ctype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8MI_H */

@@ -19,6 +19,7 @@ that tests can draw the same recipe at small shapes.
 
 from __future__ import annotations
 
+import concurrent.futures as _cf
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -58,8 +59,23 @@ class HostTensor:
 def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
     """Round fp32 values to bfloat16 (nearest, ties to even); return uint16 bits.
 
-    NaNs stay NaN (quiet bit forced), infinities stay infinite.
+    NaNs stay NaN, infinities stay infinite.  Large arrays go through PyTorch's
+    CPU conversion (the same rounding, multi-threaded); small ones through the
+    integer formula below.
     """
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if a.size < (1 << 20):
+        return _bf16_bits_small(a)
+    import torch
+    out = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():                      # keep the NaN sign and payload rule of the formula
+        out = out.copy()
+        out[nan] = _bf16_bits_small(a[nan])
+    return out
+
+
+def _bf16_bits_small(a: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
     lsb = (u >> np.uint32(16)) & np.uint32(1)
     r = ((u.astype(np.uint64) + np.uint64(0x7FFF) + lsb.astype(np.uint64)) >> np.uint64(16)).astype(np.uint32)
@@ -74,6 +90,13 @@ def _as(a32: np.ndarray, dtype: str, recipe: str, **extra) -> HostTensor:
     if dtype == "bf16":
         return HostTensor(bf16_bits_from_f32(a32), "bf16", recipe, extra)
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _parallel(fn, args_list):
+    """Run independent seeded draws on a few threads (numpy releases the GIL);
+    results come back in argument order, so the output does not depend on timing."""
+    with _cf.ThreadPoolExecutor(max_workers=min(4, len(args_list)) or 1) as ex:
+        return list(ex.map(lambda a: fn(*a), args_list))
 
 
 def _normal(shape, sigma: float, seed: int) -> np.ndarray:
@@ -130,11 +153,11 @@ def fc1_forward(tokens: int = 8192, hidden: int = 4096, ffn: int = 16384, priors
     W = _as(_normal((hidden, ffn), 0.02, s["W"]), "bf16", "N(0,0.02) seed 23")
     out = {"X": X, "W": W, "X_priors": [], "W_priors": []}
     if priors:
-        out["X_priors"] = [
-            _as(_normal_with_outliers((tokens, hidden), vs, ps), "bf16", f"X prior seeds {vs}/{ps}")
-            for vs, ps in zip(s["X_priors"], s["X_prior_outliers"])]
-        out["W_priors"] = [_as(_normal((hidden, ffn), 0.02, sd), "bf16", f"W prior seed {sd}")
-                           for sd in s["W_priors"]]
+        out["X_priors"] = _parallel(
+            lambda vs, ps: _as(_normal_with_outliers((tokens, hidden), vs, ps), "bf16", f"X prior seeds {vs}/{ps}"),
+            list(zip(s["X_priors"], s["X_prior_outliers"])))
+        out["W_priors"] = _parallel(lambda sd: _as(_normal((hidden, ffn), 0.02, sd), "bf16", f"W prior seed {sd}"),
+                                    [(sd,) for sd in s["W_priors"]])
     return out
 
 
@@ -147,10 +170,13 @@ DGRAD_SEEDS = {"dY_mag": 31, "dY_sign": 32, "W": 33,
 
 
 def _loguniform_signed(shape, mag_seed: int, sign_seed: int, lo_exp=-6.0, hi_exp=2.0) -> np.ndarray:
-    u = np.random.default_rng(mag_seed).uniform(lo_exp, hi_exp, size=shape)
-    mag = np.power(10.0, u).astype(np.float32)
-    neg = np.random.default_rng(sign_seed).integers(0, 2, size=shape, dtype=np.int8).astype(bool)
-    mag[neg] = -mag[neg]
+    u = np.random.default_rng(mag_seed).random(size=shape, dtype=np.float32)
+    u *= np.float32(hi_exp - lo_exp)
+    u += np.float32(lo_exp)
+    mag = np.power(np.float32(10.0), u)
+    neg = np.random.default_rng(sign_seed).integers(0, 2, size=shape, dtype=np.int8)
+    bits = mag.view(np.uint32)
+    np.bitwise_or(bits, neg.astype(np.uint32) << np.uint32(31), out=bits)   # sign bit set with p = 1/2
     return mag
 
 
@@ -162,10 +188,11 @@ def dgrad_hybrid(tokens: int = 8192, ffn: int = 16384, hidden: int = 4096, prior
     W = _as(_normal((ffn, hidden), 0.02, s["W"]), "bf16", "N(0,0.02) seed 33")
     out = {"dY": dY, "W": W, "dY_priors": [], "W_priors": []}
     if priors:
-        out["dY_priors"] = [_as(_loguniform_signed((tokens, ffn), sd, sd + 100), "bf16", f"dY prior {sd}/{sd + 100}")
-                            for sd in s["dY_priors"]]
-        out["W_priors"] = [_as(_normal((ffn, hidden), 0.02, sd), "bf16", f"W prior seed {sd}")
-                           for sd in s["W_priors"]]
+        out["dY_priors"] = _parallel(
+            lambda sd: _as(_loguniform_signed((tokens, ffn), sd, sd + 100), "bf16", f"dY prior {sd}/{sd + 100}"),
+            [(sd,) for sd in s["dY_priors"]])
+        out["W_priors"] = _parallel(lambda sd: _as(_normal((ffn, hidden), 0.02, sd), "bf16", f"W prior seed {sd}"),
+                                    [(sd,) for sd in s["W_priors"]])
     return out
 
 

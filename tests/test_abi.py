@@ -1,0 +1,123 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching any device.
+
+Only argument combinations that the library refuses during host-side
+validation are passed with fake pointers; nothing here can reach a kernel."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import fp8_precision_numerics_amd as fm
+from fp8_precision_numerics_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8mi.h")
+
+OK, ENULL, ESHAPE, EALIGN, EFMT, EDTYPE, ELAUNCH, EDEV = 0, -1, -2, -3, -4, -5, -6, -7
+A16 = ctypes.c_void_p(0x10000)        # 16-B aligned fake address (never dereferenced)
+A8 = ctypes.c_void_p(0x10008)         # misaligned fake address
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^FP8MI_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, re.MULTILINE)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fm.load_library()
+
+
+def test_header_declares_the_bound_symbols():
+    assert declared_symbols() == sorted(_binding.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert fm.version() == 100
+    for code in (OK, ENULL, ESHAPE, EALIGN, EFMT, EDTYPE, ELAUNCH, EDEV):
+        assert fm.status_string(code) and fm.status_string(code) != "unknown status"
+    assert fm.status_string(12345) == "unknown status"
+
+
+def test_quantize_argument_errors(lib):
+    q = lib.fp8_quantize
+    assert q(A16, 7, 4, 16, 0, A16, A16, None, None, None, None) == EDTYPE
+    assert q(A16, 0, 4, 16, 9, A16, A16, None, None, None, None) == EFMT
+    assert q(A16, 0, -1, 16, 0, A16, A16, None, None, None, None) == ESHAPE
+    assert q(A16, 0, 1 << 40, 1 << 40, 0, A16, A16, None, None, None, None) == ESHAPE
+    assert q(A16, 0, 4, 16, 0, A16, None, None, None, None, None) == ENULL      # no output at all
+    assert q(A16, 0, 4, 16, 0, None, A16, None, None, None, None) == ENULL      # cast without a scale
+    assert q(None, 0, 4, 16, 0, A16, A16, None, None, None, None) == ENULL
+    assert q(A8, 0, 4, 16, 0, A16, A16, None, None, None, None) == EALIGN
+    assert q(A16, 0, 4, 16, 0, A16, A8, None, None, None, None) == EALIGN
+    assert q(A16, 0, 4, 24, 0, A16, None, A16, None, None, None) == EALIGN      # transpose needs 16 | cols
+    assert q(A16, 0, 20, 16, 0, A16, None, A16, None, None, None) == EALIGN     # ... and 16 | rows
+    assert q(None, 0, 0, 16, 0, A16, A16, None, None, None, None) == OK         # empty, no reductions
+
+
+def test_amax_update_argument_errors(lib):
+    u = lib.fp8_amax_update
+    assert u(A16, 16, A16, A16, 5, A16, A16, None, None) == EFMT
+    assert u(None, 16, A16, A16, 0, A16, A16, None, None) == ENULL
+    assert u(A16, 16, A16, A16, 0, None, A16, None, None) == ENULL
+    assert u(A16, 0, A16, A16, 0, A16, A16, None, None) == ESHAPE
+    assert u(A16, 4097, A16, A16, 0, A16, A16, None, None) == ESHAPE
+
+
+def test_gemm_argument_errors(lib):
+    g = lib.fp8_gemm
+    assert g(A16, 3, A16, 0, 16, 16, 16, A16, A16, A16, 0, None) == EFMT
+    assert g(A16, 0, A16, 0, 16, 16, 16, A16, A16, A16, 4, None) == EDTYPE
+    assert g(A16, 0, A16, 0, 16, 16, 0, A16, A16, A16, 0, None) == ESHAPE
+    assert g(A16, 0, A16, 0, -1, 16, 16, A16, A16, A16, 0, None) == ESHAPE
+    assert g(A16, 0, A16, 0, 1 << 31, 16, 16, A16, A16, A16, 0, None) == ESHAPE
+    assert g(A16, 0, A16, 0, 16, 16, 24, A16, A16, A16, 0, None) == EALIGN     # K % 16
+    assert g(None, 0, A16, 0, 16, 16, 16, A16, A16, A16, 0, None) == ENULL
+    assert g(A16, 0, A16, 0, 16, 16, 16, None, A16, A16, 0, None) == ENULL
+    assert g(A8, 0, A16, 0, 16, 16, 16, A16, A16, A16, 0, None) == EALIGN
+    assert g(A16, 0, A16, 0, 16, 16, 16, A16, A16, A8, 0, None) == EALIGN
+    assert g(None, 0, None, 0, 0, 16, 16, None, None, None, 0, None) == OK      # M == 0 is a no-op
+
+
+def test_blockwise_and_grouped_argument_errors(lib):
+    b = lib.fp8_quantize_blockwise
+    assert b(A16, 0, 4, 128, 2, 0, A16, A16, None) == ESHAPE
+    assert b(A16, 0, 4, 120, 1, 0, A16, A16, None) == EALIGN
+    assert b(A16, 0, 4, 128, 1, 0, None, A16, None) == ENULL
+    assert b(A8, 0, 4, 128, 1, 0, A16, A16, None) == EALIGN
+    gg = lib.fp8_grouped_gemm
+    assert gg(A16, A16, A16, A16, A16, 0, 16, 16, 128, A16, 0, None) == ESHAPE
+    assert gg(A16, A16, A16, A16, A16, 2000, 16, 16, 128, A16, 0, None) == ESHAPE
+    assert gg(A16, A16, A16, A16, A16, 2, 16, 16, 120, A16, 0, None) == EALIGN
+    assert gg(A16, A16, A16, A16, None, 2, 16, 16, 128, A16, 0, None) == ENULL
+    assert gg(A16, A16, A16, A16, A16, 2, 16, 16, 128, A16, 9, None) == EDTYPE
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device path")
+def test_valid_arguments_without_a_device_report_device_error(lib):
+    assert lib.fp8_gemm(A16, 0, A16, 0, 16, 16, 16, A16, A16, A16, 0, None) == EDEV
+    assert lib.fp8_amax_update(A16, 16, A16, A16, 0, A16, A16, None, None) == EDEV
+
+
+def test_python_binding_rejects_host_tensors():
+    x = torch.zeros(4, 16)
+    with pytest.raises(ValueError):
+        fm.fp8_quantize(x, "e4m3", amax=torch.zeros(1))
+    with pytest.raises(ValueError):
+        fm.fp8_quantize(x, "e9m9", amax=torch.zeros(1))
+
+
+def test_recipe_defaults_follow_the_pages():
+    r = fm.Recipe()
+    assert (r.fmt_fwd, r.fmt_bwd, r.history_len, r.algo) == ("e4m3", "e5m2", 16, "max")
+    with pytest.raises(ValueError):
+        fm.Recipe(algo="most_recent")
