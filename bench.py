@@ -32,7 +32,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "FP8 GEMM TFLOPS (% MFMA peak) at 8192x4096x16384; cast+amax HBM GB/s"
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA, published
+PEAK_FP16_TFLOPS = 2500.0     # MI355X dense FP16/BF16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+# Matrix-core peak of the instruction each accumulation mode runs on.
+PEAK_BY_ACCUM = {"exact": PEAK_FP16_TFLOPS, "mfma_fp8": PEAK_FP8_TFLOPS}
 
 
 def log(*a):
@@ -47,6 +50,8 @@ def parse():
     p.add_argument("--quick", action="store_true", help="headline step only (no extras, no CPU baseline)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--stream-dtype", default="bf16", choices=["bf16", "f32"])
+    p.add_argument("--accum", default="exact", choices=["exact", "mfma_fp8"],
+                   help="GEMM accumulation mode of the timed step (the other mode is timed as an extra)")
     return p.parse_args()
 
 
@@ -101,11 +106,11 @@ def headline(torch, fm, args):
             with t_cw:
                 stW.quantize(W, q_t=qwT)
             with t_gemm:
-                fm.fp8_gemm(qx, "e4m3", qwT, "e4m3", stX.scale_inv, stW.scale_inv, c)
+                fm.fp8_gemm(qx, "e4m3", qwT, "e4m3", stX.scale_inv, stW.scale_inv, c, accum=args.accum)
         else:
             stX.quantize(X, q=qx)
             stW.quantize(W, q_t=qwT)
-            fm.fp8_gemm(qx, "e4m3", qwT, "e4m3", stX.scale_inv, stW.scale_inv, c)
+            fm.fp8_gemm(qx, "e4m3", qwT, "e4m3", stX.scale_inv, stW.scale_inv, c, accum=args.accum)
         stX.update()
         stW.update()
 
@@ -125,12 +130,29 @@ def headline(torch, fm, args):
     cx_ms, cw_ms = statistics.mean(t_cx.ms()), statistics.mean(t_cw.ms())
     log(f"step {total_ms / args.steps:.3f} ms; gemm {gemm_ms * 1e3:.1f} us ({flops / gemm_ms / 1e9:.0f} TFLOP/s); "
         f"cast X {cx_ms * 1e3:.1f} us; cast-transpose W {cw_ms * 1e3:.1f} us")
+    # the same GEMM in the other accumulation mode, alone
+    other = "mfma_fp8" if args.accum == "exact" else "exact"
+    t_other = EventTimer(torch)
+    for i in range(args.steps + 3):
+        if i < 3:
+            fm.fp8_gemm(qx, "e4m3", qwT, "e4m3", stX.scale_inv, stW.scale_inv, c, accum=other)
+            continue
+        with t_other:
+            fm.fp8_gemm(qx, "e4m3", qwT, "e4m3", stX.scale_inv, stW.scale_inv, c, accum=other)
+    torch.cuda.synchronize()
+    other_ms = statistics.mean(t_other.ms())
+    log(f"gemm in {other} mode: {other_ms * 1e3:.1f} us ({flops / other_ms / 1e9:.0f} TFLOP/s)")
     out = {
+        "accum": args.accum,
+        "gemm_other_mode": {"accum": other, "us": other_ms * 1e3, "tflops": flops / other_ms / 1e9,
+                            "frac_of_its_peak": flops / other_ms / 1e9 / PEAK_BY_ACCUM[other],
+                            "frac_of_fp8_peak": flops / other_ms / 1e9 / PEAK_FP8_TFLOPS},
         "ms_per_step": total_ms / args.steps,
         "value": flops / (total_ms / args.steps) / 1e9,
         "gemm_ms": gemm_ms,
         "gemm_ms_median": statistics.median(t_gemm.ms()),
         "gemm_tflops": flops / gemm_ms / 1e9,
+        "gemm_frac_of_fp8_peak": flops / gemm_ms / 1e9 / PEAK_FP8_TFLOPS,
         "cast_x_us": cx_ms * 1e3,
         "cast_x_gbs": M * K * 3 / (cx_ms * 1e-3) / 1e9,
         "cast_transpose_w_us": cw_ms * 1e3,
@@ -208,20 +230,24 @@ def dgrad_bench(torch, fm, iters=20):
         stW.quantize(W, q_t=qwT)
         stW.update()
     c = torch.empty((M, N), dtype=torch.float32, device=dev)
-    timer = EventTimer(torch)
-    for i in range(iters + 3):
-        if i < 3:
-            fm.fp8_gemm(qg, "e5m2", qwT, "e4m3", stG.scale_inv, stW.scale_inv, c)
-        else:
-            with timer:
-                fm.fp8_gemm(qg, "e5m2", qwT, "e4m3", stG.scale_inv, stW.scale_inv, c)
-    torch.cuda.synchronize()
-    ms = statistics.mean(timer.ms())
     flops = 2.0 * M * N * K
-    log(f"dgrad E5M2xE4M3 -> fp32: {ms * 1e3:.1f} us = {flops / ms / 1e9:.0f} TFLOP/s")
+    res = {}
+    for accum in ("exact", "mfma_fp8"):
+        timer = EventTimer(torch)
+        for i in range(iters + 3):
+            if i < 3:
+                fm.fp8_gemm(qg, "e5m2", qwT, "e4m3", stG.scale_inv, stW.scale_inv, c, accum=accum)
+            else:
+                with timer:
+                    fm.fp8_gemm(qg, "e5m2", qwT, "e4m3", stG.scale_inv, stW.scale_inv, c, accum=accum)
+        torch.cuda.synchronize()
+        ms = statistics.mean(timer.ms())
+        log(f"dgrad E5M2xE4M3 -> fp32 ({accum}): {ms * 1e3:.1f} us = {flops / ms / 1e9:.0f} TFLOP/s")
+        res[accum] = {"us": ms * 1e3, "tflops": flops / ms / 1e9,
+                      "frac_of_its_peak": flops / ms / 1e9 / PEAK_BY_ACCUM[accum]}
     del G, W, qg, qwT, c
     torch.cuda.empty_cache()
-    return {"us": ms * 1e3, "tflops": flops / ms / 1e9, "frac_peak": flops / ms / 1e9 / PEAK_FP8_TFLOPS}
+    return res
 
 
 def moe_bench(torch, fm, iters=20):
@@ -242,29 +268,36 @@ def moe_bench(torch, fm, iters=20):
     qb = torch.empty((G * N, K), dtype=torch.uint8, device=dev)
     sb = torch.empty((G * N // 128, K // 128), dtype=torch.float32, device=dev)
     c = torch.empty((total, N), dtype=torch.bfloat16, device=dev)
-    ta, tb, tg = EventTimer(torch), EventTimer(torch), EventTimer(torch)
+    ta, tb = EventTimer(torch), EventTimer(torch)
+    tg = {"exact": EventTimer(torch), "mfma_fp8": EventTimer(torch)}
     for i in range(iters + 3):
         if i < 3:
             fm.fp8_quantize_blockwise(A, 1, "e4m3", qa, sa)
             fm.fp8_quantize_blockwise(B, 128, "e4m3", qb, sb)
-            fm.fp8_grouped_gemm(qa, sa, qb.view(G, N, K), sb.view(G, N // 128, K // 128), offs, c)
+            for accum in tg:
+                fm.fp8_grouped_gemm(qa, sa, qb.view(G, N, K), sb.view(G, N // 128, K // 128), offs, c, accum=accum)
             continue
         with ta:
             fm.fp8_quantize_blockwise(A, 1, "e4m3", qa, sa)
         with tb:
             fm.fp8_quantize_blockwise(B, 128, "e4m3", qb, sb)
-        with tg:
-            fm.fp8_grouped_gemm(qa, sa, qb.view(G, N, K), sb.view(G, N // 128, K // 128), offs, c)
+        for accum, timer in tg.items():
+            with timer:
+                fm.fp8_grouped_gemm(qa, sa, qb.view(G, N, K), sb.view(G, N // 128, K // 128), offs, c, accum=accum)
     torch.cuda.synchronize()
-    g_ms = statistics.mean(tg.ms())
     flops = 2.0 * total * N * K
+    gem = {}
+    for accum, timer in tg.items():
+        g_ms = statistics.mean(timer.ms())
+        gem[accum] = {"us": g_ms * 1e3, "tflops": flops / g_ms / 1e9,
+                      "frac_of_its_peak": flops / g_ms / 1e9 / PEAK_BY_ACCUM[accum]}
     a_ms, b_ms = statistics.mean(ta.ms()), statistics.mean(tb.ms())
-    log(f"moe grouped: gemm {g_ms * 1e3:.1f} us = {flops / g_ms / 1e9:.0f} TFLOP/s; "
+    log(f"moe grouped: gemm exact {gem['exact']['us']:.1f} us ({gem['exact']['tflops']:.0f} TFLOP/s), "
+        f"mfma_fp8 {gem['mfma_fp8']['us']:.1f} us ({gem['mfma_fp8']['tflops']:.0f} TFLOP/s); "
         f"blockwise A {a_ms * 1e3:.1f} us, W {b_ms * 1e3:.1f} us")
     del A, B, qa, sa, qb, sb, c
     torch.cuda.empty_cache()
-    return {"token_counts": counts, "gemm_us": g_ms * 1e3, "gemm_tflops": flops / g_ms / 1e9,
-            "frac_peak": flops / g_ms / 1e9 / PEAK_FP8_TFLOPS, "blockwise_a_us": a_ms * 1e3,
+    return {"token_counts": counts, "grouped_gemm": gem, "blockwise_a_us": a_ms * 1e3,
             "blockwise_w_us": b_ms * 1e3,
             "blockwise_a_gbs": total * K * 3 / (a_ms * 1e-3) / 1e9,
             "blockwise_w_gbs": G * N * K * 3 / (b_ms * 1e-3) / 1e9}
@@ -344,10 +377,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": "fc1_forward_delayed_scaling", "M": 8192, "K": 4096, "N": 16384,
                    "inputs": "bf16 X (N(0,1), 0.1% x100 outliers), bf16 W N(0,0.02)", "fp8": "e4m3 x e4m3",
-                   "out": "bf16", "history_len": 16, "amax_rule": "max"},
-        "roofline": {"bound": "mfma", "achieved": round(head["gemm_tflops"], 1), "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(head["gemm_tflops"] / PEAK_FP8_TFLOPS, 4),
-                     "traffic": None},
+                   "out": "bf16", "history_len": 16, "amax_rule": "max", "accum": args.accum},
+        "roofline": {"bound": "mfma", "achieved": round(head["gemm_tflops"], 1),
+                     "peak": PEAK_BY_ACCUM[args.accum], "unit": "TFLOP/s",
+                     "frac": round(head["gemm_tflops"] / PEAK_BY_ACCUM[args.accum], 4),
+                     "traffic": None,
+                     "kernel": "gemm_kernel (%s accumulation: %s matrix cores)"
+                               % (args.accum, "fp16" if args.accum == "exact" else "fp8")},
         "cpu_baseline": cpu,
         "extra": extra,
     }

@@ -15,13 +15,16 @@ import os
 
 import torch
 
-__all__ = ["E4M3", "E5M2", "F32", "BF16", "Fp8Error", "load_library", "library_path",
+__all__ = ["E4M3", "E5M2", "F32", "BF16", "ACCUM_EXACT", "ACCUM_MFMA_FP8", "Fp8Error", "load_library", "library_path",
            "status_string", "version", "fp8_quantize", "fp8_amax_update", "fp8_gemm",
            "fp8_quantize_blockwise", "fp8_grouped_gemm", "EXPORTED_SYMBOLS"]
 
 E4M3, E5M2 = 0, 1
 F32, BF16 = 0, 1
+ACCUM_EXACT, ACCUM_MFMA_FP8 = 0, 1
 FORMATS = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
+ACCUMS = {"exact": ACCUM_EXACT, "mfma_fp8": ACCUM_MFMA_FP8, ACCUM_EXACT: ACCUM_EXACT,
+          ACCUM_MFMA_FP8: ACCUM_MFMA_FP8}
 
 EXPORTED_SYMBOLS = ("fp8mi_status_string", "fp8mi_version", "fp8_quantize", "fp8_amax_update",
                     "fp8_gemm", "fp8_quantize_blockwise", "fp8_grouped_gemm")
@@ -61,11 +64,12 @@ def load_library():
     lib.fp8_quantize.restype = ctypes.c_int
     lib.fp8_amax_update.argtypes = [vp, i32, vp, vp, ctypes.c_int, vp, vp, vp, vp]
     lib.fp8_amax_update.restype = ctypes.c_int
-    lib.fp8_gemm.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, ctypes.c_int, vp]
+    lib.fp8_gemm.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, ctypes.c_int,
+                             ctypes.c_int, vp]
     lib.fp8_gemm.restype = ctypes.c_int
     lib.fp8_quantize_blockwise.argtypes = [vp, ctypes.c_int, i64, i64, i32, ctypes.c_int, vp, vp, vp]
     lib.fp8_quantize_blockwise.restype = ctypes.c_int
-    lib.fp8_grouped_gemm.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, ctypes.c_int, vp]
+    lib.fp8_grouped_gemm.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, ctypes.c_int, ctypes.c_int, vp]
     lib.fp8_grouped_gemm.restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -100,6 +104,13 @@ def _xtype(x: torch.Tensor) -> int:
     if x.dtype == torch.bfloat16:
         return BF16
     raise TypeError(f"input dtype must be float32 or bfloat16, got {x.dtype}")
+
+
+def _accum(a) -> int:
+    try:
+        return ACCUMS[a]
+    except KeyError:
+        raise ValueError(f"unknown accumulation mode {a!r}") from None
 
 
 def _fmt(f) -> int:
@@ -176,8 +187,12 @@ def fp8_amax_update(history, head, amax, fmt, scale, scale_inv, status=None, str
                                                      _stream(stream)))
 
 
-def fp8_gemm(a, fa, b, fb, sinv_a, sinv_b, c, stream=None) -> None:
-    """C[M x N] = (A[M x K] · B[N x K]ᵀ) · sinv_a · sinv_b with FP8 codes A, B."""
+def fp8_gemm(a, fa, b, fb, sinv_a, sinv_b, c, accum="exact", stream=None) -> None:
+    """C[M x N] = (A[M x K] · B[N x K]ᵀ) · sinv_a · sinv_b with FP8 codes A, B.
+
+    accum: "exact" (every product exact, fp32 sums) or "mfma_fp8" (native FP8
+    matrix cores; see include/fp8mi.h for their arithmetic).
+    """
     lib = load_library()
     dev = a.device
     _check(a, "a", torch.uint8, None, dev)
@@ -192,7 +207,7 @@ def fp8_gemm(a, fa, b, fb, sinv_a, sinv_b, c, stream=None) -> None:
     ctype = F32 if c.dtype == torch.float32 else BF16
     with torch.cuda.device(dev):
         _call("fp8_gemm", lib.fp8_gemm(_p(a), _fmt(fa), _p(b), _fmt(fb), M, N, K, _p(sinv_a), _p(sinv_b),
-                                       _p(c), ctype, _stream(stream)))
+                                       _p(c), ctype, _accum(accum), _stream(stream)))
 
 
 def fp8_quantize_blockwise(x, block_rows, fmt, q, scale_inv, stream=None) -> None:
@@ -210,7 +225,7 @@ def fp8_quantize_blockwise(x, block_rows, fmt, q, scale_inv, stream=None) -> Non
                                                                    _stream(stream)))
 
 
-def fp8_grouped_gemm(a, sinv_a, b, sinv_b, m_offsets, c, stream=None) -> None:
+def fp8_grouped_gemm(a, sinv_a, b, sinv_b, m_offsets, c, accum="exact", stream=None) -> None:
     """Grouped fine-grained GEMM: a [total_m x K], b [G x N x K], m_offsets int32 [G+1]."""
     lib = load_library()
     dev = a.device
@@ -227,4 +242,5 @@ def fp8_grouped_gemm(a, sinv_a, b, sinv_b, m_offsets, c, stream=None) -> None:
     ctype = F32 if c.dtype == torch.float32 else BF16
     with torch.cuda.device(dev):
         _call("fp8_grouped_gemm", lib.fp8_grouped_gemm(_p(a), _p(sinv_a), _p(b), _p(sinv_b), _p(m_offsets), G,
-                                                       total_m, N, K, _p(c), ctype, _stream(stream)))
+                                                       total_m, N, K, _p(c), ctype, _accum(accum),
+                                                       _stream(stream)))

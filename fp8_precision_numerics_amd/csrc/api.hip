@@ -18,6 +18,7 @@ std::atomic<int> g_device_ok[kMaxDevices];         // 0 unknown, 1 gfx950, -1 no
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool fmt_ok(int f) { return f == FP8MI_E4M3 || f == FP8MI_E5M2; }
 bool dtype_ok(int d) { return d == FP8MI_F32 || d == FP8MI_BF16; }
+bool accum_ok(int a) { return a == FP8MI_ACCUM_EXACT || a == FP8MI_ACCUM_MFMA_FP8; }
 
 int check_device() {
   int dev = -1;
@@ -58,11 +59,12 @@ const char* fp8mi_status_string(int status) {
     case FP8MI_ERR_DTYPE: return "unknown data type";
     case FP8MI_ERR_LAUNCH: return "kernel launch failed";
     case FP8MI_ERR_DEVICE: return "no usable gfx950 device is current";
+    case FP8MI_ERR_ACCUM: return "unknown accumulation mode";
     default: return "unknown status";
   }
 }
 
-int fp8mi_version(void) { return 100; }
+int fp8mi_version(void) { return 200; }
 
 int fp8_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, const float* scale,
                  uint8_t* q, uint8_t* q_t, float* amax, unsigned long long* sat, void* stream) {
@@ -96,9 +98,10 @@ int fp8_amax_update(float* history, int32_t history_len, int32_t* head, const fl
 }
 
 int fp8_gemm(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t M, int64_t N, int64_t K,
-             const float* sinv_a, const float* sinv_b, void* C, int ctype, void* stream) {
+             const float* sinv_a, const float* sinv_b, void* C, int ctype, int accum, void* stream) {
   if (!fmt_ok(fa) || !fmt_ok(fb)) return FP8MI_ERR_FORMAT;
   if (!dtype_ok(ctype)) return FP8MI_ERR_DTYPE;
+  if (!accum_ok(accum)) return FP8MI_ERR_ACCUM;
   if (M < 0 || N < 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8MI_ERR_SHAPE;
   if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N)) return FP8MI_ERR_SHAPE;
   if ((K & 15) != 0) return FP8MI_ERR_ALIGN;
@@ -108,7 +111,7 @@ int fp8_gemm(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t M, int6
   if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return FP8MI_ERR_ALIGN;
   const int dev = check_device();
   if (dev != FP8MI_OK) return dev;
-  return launched(fp8mi::launch_gemm(A, fa, B, fb, M, N, K, sinv_a, sinv_b, C, ctype,
+  return launched(fp8mi::launch_gemm(A, fa, B, fb, M, N, K, sinv_a, sinv_b, C, ctype, accum,
                                      (hipStream_t)stream));
 }
 
@@ -132,8 +135,9 @@ int fp8_quantize_blockwise(const void* x, int xtype, int64_t rows, int64_t cols,
 
 int fp8_grouped_gemm(const uint8_t* A, const float* sinv_a, const uint8_t* B, const float* sinv_b,
                      const int32_t* m_offsets, int32_t G, int64_t total_m, int64_t N, int64_t K,
-                     void* C, int ctype, void* stream) {
+                     void* C, int ctype, int accum, void* stream) {
   if (!dtype_ok(ctype)) return FP8MI_ERR_DTYPE;
+  if (!accum_ok(accum)) return FP8MI_ERR_ACCUM;
   if (G < 1 || G > 1024) return FP8MI_ERR_SHAPE;
   if (total_m < 0 || N < 0 || K <= 0 || total_m > kMaxDim || N > kMaxDim || K > kMaxDim)
     return FP8MI_ERR_SHAPE;
@@ -147,7 +151,7 @@ int fp8_grouped_gemm(const uint8_t* A, const float* sinv_a, const uint8_t* B, co
   const int dev = check_device();
   if (dev != FP8MI_OK) return dev;
   return launched(fp8mi::launch_grouped_gemm(A, sinv_a, B, sinv_b, m_offsets, G, total_m, N, K, C,
-                                             ctype, (hipStream_t)stream));
+                                             ctype, accum, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -3,13 +3,15 @@
 // FP8 encoding follows "4.2 Hopper I — Transformer Engine·FP8" §4.2.4
 // (round_to_fp8 of the scaled tensor; large values saturate) on the OCP
 // formats the page names in §4.2.8.  The conversion itself is the gfx950
-// V_CVT_PK_FP8_F32 / V_CVT_PK_BF8_F32 instruction (OCP E4M3 / E5M2, round to
-// nearest even); around it the code fixes every edge the instruction might
-// treat differently from the rule:
-//   * |p| > max and +-Inf are clamped to +-max before the conversion (saturate),
-//   * the sign bit of the input is forced onto the code (so -0 and negative
-//     underflow give 0x80),
-//   * NaN inputs give exactly sign|0x7F.
+// V_CVT_PK_FP8_F32 / V_CVT_PK_BF8_F32 instruction (OCP E4M3 / E5M2).  Checked
+// against the CPU oracle on every bf16 bit pattern (and on the same patterns
+// scaled into the subnormal range), the instruction already rounds to
+// nearest even with gradual underflow and keeps the sign of zero; it differs
+// from the rule only on
+//   * values beyond max and +-Inf (E4M3 gives a NaN code, E5M2 an Inf code):
+//     the input is clamped to [-max, max] first (one V_MED3_F32), and
+//   * NaN (it returns one fixed code): NaN inputs are rewritten to sign|0x7F
+//     on a separate path that only runs when a NaN is present.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -66,7 +68,19 @@ __device__ __forceinline__ uint32_t cvt_pk(float a, float b, uint32_t old) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, HI);
 }
 
-// Encode four fp32 values (already scaled) into four FP8 codes, byte i = value i.
+template <int FMT>
+__device__ __forceinline__ float clamp_to_max(float p) {
+  return __builtin_amdgcn_fmed3f(p, -Fp8Traits<FMT>::max_value, Fp8Traits<FMT>::max_value);
+}
+
+// Encode four scaled fp32 values that are known not to be NaN: byte i = value i.
+template <int FMT>
+__device__ __forceinline__ uint32_t encode4_finite(float p0, float p1, float p2, float p3) {
+  const uint32_t w = cvt_pk<FMT, false>(clamp_to_max<FMT>(p0), clamp_to_max<FMT>(p1), 0u);
+  return cvt_pk<FMT, true>(clamp_to_max<FMT>(p2), clamp_to_max<FMT>(p3), w);
+}
+
+// Encode four scaled fp32 values of any kind (the full rule, NaN included).
 template <int FMT>
 __device__ __forceinline__ uint32_t encode4(float p0, float p1, float p2, float p3) {
   uint32_t w = cvt_pk<FMT, false>(sat_clamp<FMT>(p0), sat_clamp<FMT>(p1), 0u);

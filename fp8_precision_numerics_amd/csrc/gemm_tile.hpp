@@ -1,33 +1,74 @@
 // Shared building blocks of the FP8 GEMM kernels (dense and grouped).
 //
-// Matrix-core contraction: V_MFMA_F32_16X16X128_F8F6F4 (gfx950).  One
-// instruction multiplies a 16x128 FP8 block by a 128x16 FP8 block and adds an
-// fp32 16x16 block; the two operand formats (E4M3 / E5M2) are chosen per
-// operand.  Lane l of the wave supplies row (l % 16) and the 32-byte K slice
-// (l / 16) of each operand; the fp32 result lands in lane l as column (l % 16),
-// rows 4*(l/16) .. 4*(l/16)+3.  The kernels feed the B tile (rows = n) as the
-// instruction's first operand and the A tile (rows = m) as its second, so the
-// result block is C^T: lane l holds row m = l % 16 and FOUR CONSECUTIVE
-// columns n = 4*(l/16) .. +3 — a contiguous 8-B (bf16) / 16-B (fp32) store.
+// Two ways to contract FP8 operands on gfx950 (selected per call):
+//
+// * kAccumExact — every product exact, sums in fp32.  The FP8 codes are
+//   widened in registers to fp16 (exact for both E4M3 and E5M2, subnormals
+//   included: V_CVT_SCALEF32_PK_F16_FP8/BF8 with scale 1) and contracted with
+//   V_MFMA_F32_16X16X32_F16.  This is "GEMM in FP8, FP32 accumulation" in the
+//   sense of "4.2 Hopper I — Transformer Engine·FP8" §4.2.4: the result
+//   meets 1e-5·Σ|ab| for every input.
+//
+// * kAccumMfma8 — the native FP8 matrix-core instruction
+//   V_MFMA_F32_16X16X128_F8F6F4.  Measured on MI355X: it forms dot products of
+//   8 consecutive K terms in fixed point whose last bit lies 13 bits below
+//   the largest product of the 8, truncating the rest toward zero, and adds
+//   those partials in fp32.  Twice the rate of the fp16 path; the per-group
+//   truncation (at most 8·2^-13 of the group's largest product) is its
+//   accuracy price.
+//
+// Operand lanes: lane l of the wave supplies row (l % 16) of each operand and
+// the 32-byte K slice (l / 16) of the 128-deep K step.  The kernels feed the B
+// tile (rows = n) as the instruction's first operand and the A tile (rows = m)
+// as its second, so the 16x16 result block is Cᵀ: lane l holds row
+// m = l % 16 and FOUR CONSECUTIVE columns n = 4*(l/16) .. +3, which the
+// epilogue stores as one 8-B (bf16) / 16-B (fp32) vector.  The fp16 path uses
+// bytes [8s, 8s+8) of the same 32-byte slice for its K sub-step s = 0..3:
+// any assignment of K values to (lane, register) slots works as long as both
+// operands use the same one.
 //
 // Operand tiles live in LDS as rows of 128 bytes (one K step).  The 16-byte
-// granule g of row r is stored at granule position g ^ (r & 7): the 16-B reads
-// of a fragment (rows r..r+15, same granule) and the 16-B writes of a loaded
-// row both touch eight different granule positions per eight lanes.
+// granule g of row r is stored at granule position g ^ (r & 7): the 16-B
+// reads of a fragment (rows r..r+15, same granule) and the loads of eight
+// rows per wave instruction both spread over all granule positions.
 #pragma once
 
 #include "device_common.hpp"
 
 namespace fp8mi {
 
-constexpr int kBK = 128;  // K bytes per main-loop step (one MFMA deep)
+constexpr int kBK = 128;  // K bytes per main-loop step
+enum : int { kAccumExact = 0, kAccumMfma8 = 1 };
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void global_void_t;
 
 __device__ __forceinline__ int lds_granule(int row, int g) { return row * kBK + (((g ^ row) & 7) << 4); }
 
 template <int FA, int FB>
-__device__ __forceinline__ v4f mfma16(const v8i& first, const v8i& second, const v4f& c) {
+__device__ __forceinline__ v4f mfma_fp8(const v8i& first, const v8i& second, const v4f& c) {
   // Scale operands are zero, which selects the plain (unscaled) instruction.
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, FA, FB, 0, 0, 0, 0);
+}
+
+// Eight FP8 codes (bytes of w0 then w1) widened exactly to fp16.
+template <int F>
+__device__ __forceinline__ v8h widen8(uint32_t w0, uint32_t w1) {
+  v2h a, b, c, d;
+  if constexpr (F == kE4M3) {
+    a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+    b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+    c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+    d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  } else {
+    a = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w0, 1.0f, false);
+    b = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w0, 1.0f, true);
+    c = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w1, 1.0f, false);
+    d = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w1, 1.0f, true);
+  }
+  return (v8h){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // Read the 32-byte K slice of one fragment row for this lane from an LDS tile.
@@ -40,6 +81,51 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int lane) 
   r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
   return r;
 }
+
+// Move ROWS x 128 bytes (rows row0.. of a row-major byte matrix with row
+// stride ld, column offset k0) into an LDS tile with direct-to-LDS loads: one
+// wave instruction fills 8 rows (1 KiB; lane i writes bytes [16i, 16i+16) of
+// it), so lane i fetches granule (i & 7) ^ (i >> 3) of row i >> 3.  Rows past
+// `rows_valid` are clamped to the last valid row: they only feed output rows
+// or columns that are never stored.  The caller waits for vmcnt before use.
+template <int ROWS, int NW>
+__device__ __forceinline__ void tile_load_direct(const uint8_t* __restrict__ base, int64_t ld,
+                                                 int64_t row0, int64_t rows_valid, int k0,
+                                                 uint8_t* lds_tile, int wave, int lane) {
+  constexpr int GROUPS = ROWS / 8;
+  static_assert(GROUPS % NW == 0, "tile rows must split evenly over the wavefronts");
+  const int r_in = lane >> 3;
+  const int g = (lane & 7) ^ r_in;
+#pragma unroll
+  for (int q = 0; q < GROUPS / NW; ++q) {
+    const int grp = wave + q * NW;
+    int64_t r = row0 + grp * 8 + r_in;
+    r = r < rows_valid ? r : rows_valid - 1;
+    const uint8_t* src = base + r * ld + k0 + g * 16;
+    __builtin_amdgcn_global_load_lds((global_void_t*)src, (lds_void_t*)(lds_tile + grp * 1024), 16, 0, 0);
+  }
+}
+
+// Same tile, staged through registers with zero fill for k >= K (the ragged
+// last K step) and for rows past the edge.
+template <int ROWS, int NT>
+__device__ __forceinline__ void tile_load_zero_fill(const uint8_t* __restrict__ base, int64_t ld,
+                                                    int64_t row0, int64_t rows_valid, int k0, int K,
+                                                    uint8_t* lds_tile, int t) {
+  constexpr int PER = ROWS * 8 / NT;
+  const int g = t & 7;
+  const int k = k0 + g * 16;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int row = (t >> 3) + j * (NT / 8);
+    const int64_t r = row0 + row;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < rows_valid && k < K) v = *reinterpret_cast<const uint4*>(base + r * ld + k);
+    *reinterpret_cast<uint4*>(lds_tile + lds_granule(row, g)) = v;
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Map a linear workgroup id to an output tile.  Workgroups are dealt to the
 // 8 XCDs round-robin (id % 8); remap so each XCD receives a contiguous range
@@ -88,6 +174,39 @@ __device__ __forceinline__ void store4(void* C, int64_t N, int64_t m, int64_t n,
       if (n + 1 < N) c[1] = lo[1];
       if (n + 2 < N) c[2] = hi[0];
       if (n + 3 < N) c[3] = hi[1];
+    }
+  }
+}
+
+// One 128-deep K step of a WTM x WTN wave tile: acc[i][j] += A_i · B_jᵀ.
+template <int FM, int FN, int FA, int FB, int MODE>
+__device__ __forceinline__ void wave_kstep(const uint8_t* sa, const uint8_t* sb, int a_row0, int b_row0,
+                                           int lane, v4f (&acc)[FM][FN]) {
+  v8i bf[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) bf[j] = lds_frag(sb, b_row0 + j * 16 + (lane & 15), lane);
+  if constexpr (MODE == kAccumMfma8) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const v8i af = lds_frag(sa, a_row0 + i * 16 + (lane & 15), lane);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma_fp8<FB, FA>(bf[j], af, acc[i][j]);
+    }
+  } else {
+    v8i af[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[i] = lds_frag(sa, a_row0 + i * 16 + (lane & 15), lane);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v8h bh[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bh[j] = widen8<FB>((uint32_t)bf[j][2 * s], (uint32_t)bf[j][2 * s + 1]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const v8h ah = widen8<FA>((uint32_t)af[i][2 * s], (uint32_t)af[i][2 * s + 1]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bh[j], ah, acc[i][j], 0, 0, 0);
+      }
     }
   }
 }

@@ -3,15 +3,19 @@
 //
 // "4.2 Hopper I — Transformer Engine·FP8", §4.2.4: the FP8 tensor is
 // round_to_fp8(tensor × scale) with scale ≈ FP8_MAX / amax; delayed scaling
-// lets the cast use a scale known before the pass, so amax of this step and
+// lets the cast use a scale known before the pass, so this step's amax and
 // the cast come out of ONE read of the tensor.  "FP8 and low-precision
 // formats", "Deep dive": scale factors are per tensor or per block.
 //
 // The per-tensor kernels are HBM-bound: per element they read 2 B (bf16) or
-// 4 B (fp32) and write 1 B (2 B with the transposed copy).  Loads and stores are
-// 16-B vectors; amax is an integer max over |bits| (exact and order-free),
-// reduced across the wavefront with cross-lane shuffles, across the workgroup
-// through LDS, and across workgroups with one atomicMax per workgroup.
+// 4 B (fp32) and write 1 B (2 B with both layouts).  Every wave instruction
+// moves one contiguous 1 KiB of input (16 B per lane).  Per element the work
+// is: widen, multiply by the scale, clamp (V_MED3_F32), half a packed
+// conversion, and an integer max of |bits| for amax (exact and order-free);
+// NaN codes are fixed on a separate path taken only when a NaN is present.
+// amax is reduced across the wavefront with shuffles, across the workgroup in
+// LDS, and across workgroups with one atomicMax per workgroup; the
+// saturation count is a wave ballot + popcount.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -19,6 +23,9 @@ namespace fp8mi {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 __global__ void zero_outputs_kernel(uint32_t* amax_bits, unsigned long long* sat) {
   if (threadIdx.x == 0) {
@@ -27,24 +34,23 @@ __global__ void zero_outputs_kernel(uint32_t* amax_bits, unsigned long long* sat
   }
 }
 
-// Reduce (amax, count) over the workgroup and fold into the global outputs.
-__device__ __forceinline__ void block_finish(uint32_t amx, uint32_t cnt, uint32_t* amax_bits,
+// Fold (per-lane amax bits, per-wave saturation count) into the global outputs.
+__device__ __forceinline__ void block_finish(uint32_t amx, uint32_t wave_cnt, uint32_t* amax_bits,
                                              unsigned long long* sat) {
-  __shared__ uint32_t s_max[kThreads / 64];
-  __shared__ uint32_t s_cnt[kThreads / 64];
+  __shared__ uint32_t s_max[kWaves];
+  __shared__ uint32_t s_cnt[kWaves];
   amx = wave_max_u32(amx);
-  cnt = wave_sum_u32(cnt);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
     s_max[wave] = amx;
-    s_cnt[wave] = cnt;
+    s_cnt[wave] = wave_cnt;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t m = s_max[0];
     unsigned long long c = s_cnt[0];
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) {
+    for (int w = 1; w < kWaves; ++w) {
       m = m > s_max[w] ? m : s_max[w];
       c += s_cnt[w];
     }
@@ -53,18 +59,34 @@ __device__ __forceinline__ void block_finish(uint32_t amx, uint32_t cnt, uint32_
   }
 }
 
-// Load 8 consecutive input elements (16 B of bf16 or 32 B of fp32) as fp32.
+// With a finite non-zero scale, x * s is NaN exactly where x is NaN.
+__device__ __forceinline__ bool scale_is_regular(float s) {
+  const uint32_t m = f2u(s) & 0x7FFFFFFFu;
+  return m != 0u && m < 0x7F800000u;
+}
+
+// One 16-B input vector: 8 bf16 or 4 fp32 elements.
 template <int XT>
-__device__ __forceinline__ void load8(const void* __restrict__ x, int64_t elem, float v[8]) {
+struct Vec {
+  static constexpr int EPV = XT == kBF16 ? 8 : 4;
+};
+
+// Load vector `vi` as fp32 values and the max of its magnitude bit patterns.
+template <int XT>
+__device__ __forceinline__ void load_vec(const void* __restrict__ x, int64_t vi, float* v, uint32_t& vmax) {
+  const uint4 a = reinterpret_cast<const uint4*>(x)[vi];
   if constexpr (XT == kBF16) {
-    const uint4 a = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + elem);
     v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
     v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+    const us2 m0 = __builtin_bit_cast(us2, a.x & 0x7FFF7FFFu), m1 = __builtin_bit_cast(us2, a.y & 0x7FFF7FFFu);
+    const us2 m2 = __builtin_bit_cast(us2, a.z & 0x7FFF7FFFu), m3 = __builtin_bit_cast(us2, a.w & 0x7FFF7FFFu);
+    const us2 m = __builtin_elementwise_max(__builtin_elementwise_max(m0, m1), __builtin_elementwise_max(m2, m3));
+    vmax = (uint32_t)(m[0] > m[1] ? m[0] : m[1]) << 16;
   } else {
-    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + elem);
-    const uint4 a = p[0], b = p[1];
     v[0] = u2f(a.x); v[1] = u2f(a.y); v[2] = u2f(a.z); v[3] = u2f(a.w);
-    v[4] = u2f(b.x); v[5] = u2f(b.y); v[6] = u2f(b.z); v[7] = u2f(b.w);
+    const uint32_t m01 = (a.x & 0x7FFFFFFFu) > (a.y & 0x7FFFFFFFu) ? (a.x & 0x7FFFFFFFu) : (a.y & 0x7FFFFFFFu);
+    const uint32_t m23 = (a.z & 0x7FFFFFFFu) > (a.w & 0x7FFFFFFFu) ? (a.z & 0x7FFFFFFFu) : (a.w & 0x7FFFFFFFu);
+    vmax = m01 > m23 ? m01 : m23;
   }
 }
 
@@ -76,80 +98,111 @@ __device__ __forceinline__ float load1(const void* __restrict__ x, int64_t elem)
     return reinterpret_cast<const float*>(x)[elem];
 }
 
-// amax / saturation / cast of 8 values held in registers; returns the 8 codes.
+// Scale and encode 4 values; `finite` = no NaN can appear in the products.
+// When SAT, adds the wave's count of |p| > max (NaN never counts) to wave_cnt.
 template <int FMT, bool SAT>
-__device__ __forceinline__ uint2 cast8(const float v[8], float s, uint32_t& amx, uint32_t& cnt) {
-  float p[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t m = f2u(v[i]) & 0x7FFFFFFFu;
-    amx = amx > m ? amx : m;
-    p[i] = v[i] * s;
-    if constexpr (SAT) cnt += is_saturated<FMT>(p[i]);
+__device__ __forceinline__ uint32_t scale_encode4(const float* v, float s, bool finite, uint32_t& wave_cnt) {
+  const float p0 = v[0] * s, p1 = v[1] * s, p2 = v[2] * s, p3 = v[3] * s;
+  if constexpr (SAT) {
+    constexpr float mx = Fp8Traits<FMT>::max_value;
+    wave_cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(__builtin_fabsf(p0) > mx)) +
+                __builtin_popcountll(__builtin_amdgcn_ballot_w64(__builtin_fabsf(p1) > mx)) +
+                __builtin_popcountll(__builtin_amdgcn_ballot_w64(__builtin_fabsf(p2) > mx)) +
+                __builtin_popcountll(__builtin_amdgcn_ballot_w64(__builtin_fabsf(p3) > mx));
   }
-  return make_uint2(encode4<FMT>(p[0], p[1], p[2], p[3]), encode4<FMT>(p[4], p[5], p[6], p[7]));
+  if (__builtin_expect(finite, 1)) return encode4_finite<FMT>(p0, p1, p2, p3);
+  return encode4<FMT>(p0, p1, p2, p3);
 }
 
 // ---------------------------------------------------------------------------
-// Flat kernel: q (row-major) and/or amax; each thread owns 16-element chunks.
+// Flat kernel: q (row-major) and/or amax.  Each lane casts U vectors; vector u
+// of a wave covers one contiguous 1 KiB (64 lanes x 16 B).
 // ---------------------------------------------------------------------------
+constexpr int kVecPerLane = 4;
+
 template <int XT, int FMT, bool WQ, bool SAT>
 __global__ __launch_bounds__(kThreads) void quantize_flat_kernel(
     const void* __restrict__ x, int64_t n, const float* __restrict__ scale, uint8_t* __restrict__ q,
     uint32_t* __restrict__ amax_bits, unsigned long long* __restrict__ sat) {
+  constexpr int EPV = Vec<XT>::EPV, U = kVecPerLane;
   const float s = (WQ || SAT) ? *scale : 1.0f;
-  uint32_t amx = 0u, cnt = 0u;
-  const int64_t nchunk = n >> 4;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  // Two chunks per trip so that each thread keeps 4 (bf16) or 8 (fp32) 16-B loads in flight.
-  for (; c + stride < nchunk; c += 2 * stride) {
-    float v0[8], v1[8], v2[8], v3[8];
-    load8<XT>(x, c * 16, v0);
-    load8<XT>(x, c * 16 + 8, v1);
-    load8<XT>(x, (c + stride) * 16, v2);
-    load8<XT>(x, (c + stride) * 16 + 8, v3);
-    const uint2 a = cast8<FMT, SAT>(v0, s, amx, cnt);
-    const uint2 b = cast8<FMT, SAT>(v1, s, amx, cnt);
-    const uint2 d = cast8<FMT, SAT>(v2, s, amx, cnt);
-    const uint2 e = cast8<FMT, SAT>(v3, s, amx, cnt);
-    if constexpr (WQ) {
-      reinterpret_cast<uint4*>(q)[c] = make_uint4(a.x, a.y, b.x, b.y);
-      reinterpret_cast<uint4*>(q)[c + stride] = make_uint4(d.x, d.y, e.x, e.y);
+  const bool regular = scale_is_regular(s);
+  const int64_t nvec = n / EPV;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t wave_base = ((int64_t)blockIdx.x * kWaves + wave) * (64 * U);
+  uint32_t amx = 0u, wcnt = 0u;
+  float v[U][EPV];
+  uint32_t vm[U];
+  auto cast_store = [&](int u, int64_t vi) {
+    amx = amx > vm[u] ? amx : vm[u];
+    if constexpr (WQ || SAT) {
+      const bool finite = regular && vm[u] <= 0x7F800000u;
+      const uint32_t c0 = scale_encode4<FMT, SAT>(&v[u][0], s, finite, wcnt);
+      if constexpr (EPV == 8) {
+        const uint32_t c1 = scale_encode4<FMT, SAT>(&v[u][4], s, finite, wcnt);
+        if constexpr (WQ) reinterpret_cast<uint2*>(q)[vi] = make_uint2(c0, c1);
+      } else {
+        if constexpr (WQ) reinterpret_cast<uint32_t*>(q)[vi] = c0;
+      }
+    }
+  };
+  if (wave_base + U * 64 <= nvec) {
+    // Whole wave in range (all but the last wave): every load issued before any use.
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_vec<XT>(x, wave_base + u * 64 + lane, v[u], vm[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) cast_store(u, wave_base + u * 64 + lane);
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t vi = wave_base + u * 64 + lane;
+      vm[u] = 0u;
+      if (vi < nvec) load_vec<XT>(x, vi, v[u], vm[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t vi = wave_base + u * 64 + lane;
+      if (vi < nvec) cast_store(u, vi);
     }
   }
-  if (c < nchunk) {
-    float v0[8], v1[8];
-    load8<XT>(x, c * 16, v0);
-    load8<XT>(x, c * 16 + 8, v1);
-    const uint2 a = cast8<FMT, SAT>(v0, s, amx, cnt);
-    const uint2 b = cast8<FMT, SAT>(v1, s, amx, cnt);
-    if constexpr (WQ) reinterpret_cast<uint4*>(q)[c] = make_uint4(a.x, a.y, b.x, b.y);
-  }
-  // Ragged tail (n % 16 elements), element by element.
-  if (blockIdx.x == 0 && threadIdx.x < (int)(n & 15)) {
-    const int64_t i = (nchunk << 4) + threadIdx.x;
-    const float v = load1<XT>(x, i);
-    const uint32_t m = f2u(v) & 0x7FFFFFFFu;
+  // Ragged tail (n % EPV elements), element by element, in the last workgroup.
+  const int rem = (int)(n - nvec * EPV);
+  if (blockIdx.x == gridDim.x - 1 && (int)threadIdx.x < rem) {
+    const int64_t i = nvec * EPV + threadIdx.x;
+    const float xv = load1<XT>(x, i);
+    const uint32_t m = f2u(xv) & 0x7FFFFFFFu;
     amx = amx > m ? amx : m;
-    const float p = v * s;
-    if constexpr (SAT) cnt += is_saturated<FMT>(p);
+    const float p = xv * s;
+    if constexpr (SAT) {
+      wcnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(__builtin_fabsf(p) > Fp8Traits<FMT>::max_value));
+    }
     if constexpr (WQ) q[i] = encode1<FMT>(p);
   }
-  block_finish(amx, cnt, amax_bits, sat);
+  block_finish(amx, wcnt, amax_bits, sat);
 }
 
 // ---------------------------------------------------------------------------
-// Cast-transpose kernel: one 128x128 input tile per workgroup; writes q_t
-// (and q when asked).  Codes pass through LDS as a [128 col][128 row] byte
-// tile whose 16-B granules are XOR-swizzled by (col / 8) % 8 so that both the
-// byte scatter and the 16-B row reads spread over the LDS banks.
-// Requires rows % 16 == 0 and cols % 16 == 0.
+// Cast-transpose kernel: one 128x128 input tile per workgroup; writes q_t (and
+// q when asked).  Phase 1 casts the tile and writes the codes row-major into
+// LDS (row pitch 132 B); phase 2 gives each lane 4 columns x 16 rows: 16 LDS
+// words, a 4x4 byte transpose per 4 rows with V_PERM_B32, and four 16-B
+// stores into 4 rows of q_t (eight lanes cover 128 contiguous bytes of one
+// q_t row).  Requires rows % 16 == 0 and cols % 16 == 0.
 // ---------------------------------------------------------------------------
 constexpr int kTile = 128;
+constexpr int kPitch = 132;
 
-__device__ __forceinline__ int lds_t_offset(int col, int row) {
-  return col * kTile + ((((row >> 4) ^ (col >> 3)) & 7) << 4) + (row & 15);
+__device__ __forceinline__ void transpose4x4(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, uint32_t& c0,
+                                             uint32_t& c1, uint32_t& c2, uint32_t& c3) {
+  // w_r holds columns 0..3 of row r (byte k = column k); c_k gets rows 0..3 of column k.
+  const uint32_t t0 = __builtin_amdgcn_perm(w1, w0, 0x05010400u);  // w0.b0 w1.b0 w0.b1 w1.b1
+  const uint32_t t1 = __builtin_amdgcn_perm(w3, w2, 0x05010400u);  // w2.b0 w3.b0 w2.b1 w3.b1
+  const uint32_t t2 = __builtin_amdgcn_perm(w1, w0, 0x07030602u);  // w0.b2 w1.b2 w0.b3 w1.b3
+  const uint32_t t3 = __builtin_amdgcn_perm(w3, w2, 0x07030602u);  // w2.b2 w3.b2 w2.b3 w3.b3
+  c0 = __builtin_amdgcn_perm(t1, t0, 0x05040100u);
+  c1 = __builtin_amdgcn_perm(t1, t0, 0x07060302u);
+  c2 = __builtin_amdgcn_perm(t3, t2, 0x05040100u);
+  c3 = __builtin_amdgcn_perm(t3, t2, 0x07060302u);
 }
 
 template <int XT, int FMT, bool WQ, bool SAT>
@@ -157,45 +210,93 @@ __global__ __launch_bounds__(kThreads) void quantize_transpose_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, const float* __restrict__ scale,
     uint8_t* __restrict__ q, uint8_t* __restrict__ q_t, uint32_t* __restrict__ amax_bits,
     unsigned long long* __restrict__ sat) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kTile * kTile];
+  constexpr int EPV = Vec<XT>::EPV;
+  constexpr int VPR = kTile / EPV;          // vectors per tile row
+  constexpr int RPP = kThreads / VPR;       // tile rows per pass
+  constexpr int PASSES = kTile / RPP;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTile * kPitch];
   const float s = *scale;
+  const bool regular = scale_is_regular(s);
   const int64_t row0 = (int64_t)blockIdx.y * kTile, col0 = (int64_t)blockIdx.x * kTile;
   const int t = threadIdx.x;
-  const int cc8 = (t & 15) * 8;  // column offset of this thread's 8 elements
-  uint32_t amx = 0u, cnt = 0u;
-#pragma unroll 2
-  for (int i = 0; i < kTile / 16; ++i) {
-    const int rr = i * 16 + (t >> 4);
-    const int64_t r = row0 + rr, c = col0 + cc8;
-    if (r < rows && c < cols) {
-      float v[8];
-      load8<XT>(x, r * cols + c, v);
-      const uint2 w = cast8<FMT, SAT>(v, s, amx, cnt);
-      if constexpr (WQ) *reinterpret_cast<uint2*>(q + r * cols + c) = w;
+  const int vi = t % VPR, rr0 = t / VPR;
+  const int64_t vecs_per_row = cols / EPV;
+  uint32_t amx = 0u, wcnt = 0u;
+  float v[PASSES][EPV];
+  uint32_t vm[PASSES];
+  auto cast_pass = [&](int i) {
+    const int rr = rr0 + i * RPP;
+    const int64_t r = row0 + rr, c = col0 + vi * EPV;
+    amx = amx > vm[i] ? amx : vm[i];
+    const bool finite = regular && vm[i] <= 0x7F800000u;
+    const uint32_t c0 = scale_encode4<FMT, SAT>(&v[i][0], s, finite, wcnt);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(tile + rr * kPitch + vi * EPV);
+    dst[0] = c0;
+    if constexpr (EPV == 8) {
+      const uint32_t c1 = scale_encode4<FMT, SAT>(&v[i][4], s, finite, wcnt);
+      dst[1] = c1;
+      if constexpr (WQ) *reinterpret_cast<uint2*>(q + r * cols + c) = make_uint2(c0, c1);
+    } else {
+      if constexpr (WQ) *reinterpret_cast<uint32_t*>(q + r * cols + c) = c0;
+    }
+  };
+  if (row0 + kTile <= rows && col0 + kTile <= cols) {
+    // Interior tile: every load issued before any use.
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        tile[lds_t_offset(cc8 + j, rr)] = (uint8_t)(w.x >> (8 * j));
-        tile[lds_t_offset(cc8 + 4 + j, rr)] = (uint8_t)(w.y >> (8 * j));
-      }
+    for (int i = 0; i < PASSES; ++i)
+      load_vec<XT>(x, (row0 + rr0 + i * RPP) * vecs_per_row + (col0 + vi * EPV) / EPV, v[i], vm[i]);
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) cast_pass(i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) {
+      const int64_t r = row0 + rr0 + i * RPP, c = col0 + vi * EPV;
+      vm[i] = 0u;
+      if (r < rows && c < cols) load_vec<XT>(x, r * vecs_per_row + c / EPV, v[i], vm[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) {
+      const int64_t r = row0 + rr0 + i * RPP, c = col0 + vi * EPV;
+      if (r < rows && c < cols) cast_pass(i);
     }
   }
   __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kTile / 32; ++i) {
-    const int cc = i * 32 + (t >> 3), g = t & 7;
-    const int64_t c = col0 + cc, r = row0 + g * 16;
+  {
+    const int rg = t & 7, cq = t >> 3;
+    const int64_t c = col0 + cq * 4, r = row0 + rg * 16;
     if (c < cols && r < rows) {
-      const uint4 v = *reinterpret_cast<const uint4*>(&tile[lds_t_offset(cc, g * 16)]);
-      *reinterpret_cast<uint4*>(q_t + c * rows + r) = v;
+      uint32_t w[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) w[j] = *reinterpret_cast<const uint32_t*>(tile + (rg * 16 + j) * kPitch + cq * 4);
+      uint32_t o[4][4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        transpose4x4(w[4 * b], w[4 * b + 1], w[4 * b + 2], w[4 * b + 3], o[b][0], o[b][1], o[b][2], o[b][3]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<uint4*>(q_t + (c + k) * rows + r) = make_uint4(o[0][k], o[1][k], o[2][k], o[3][k]);
     }
   }
-  block_finish(amx, cnt, amax_bits, sat);
+  block_finish(amx, wcnt, amax_bits, sat);
 }
 
 // ---------------------------------------------------------------------------
 // Per-block current scaling.
-// 1 x 128 tiles: 16 lanes per tile, 8 elements per lane.
 // ---------------------------------------------------------------------------
+// Load 8 consecutive elements (one or two 16-B vectors) and their magnitude max.
+template <int XT>
+__device__ __forceinline__ void load8(const void* __restrict__ x, int64_t elem, float v[8], uint32_t& vmax) {
+  if constexpr (XT == kBF16) {
+    load_vec<XT>(x, elem / 8, v, vmax);
+  } else {
+    uint32_t m1;
+    load_vec<XT>(x, elem / 4, v, vmax);
+    load_vec<XT>(x, elem / 4 + 1, v + 4, m1);
+    vmax = vmax > m1 ? vmax : m1;
+  }
+}
+
+// 1 x 128 tiles: 16 lanes per tile, 8 elements per lane.
 template <int XT, int FMT>
 __global__ __launch_bounds__(kThreads) void quantize_rowtile_kernel(const void* __restrict__ x,
                                                                     int64_t rows, int64_t cols,
@@ -207,24 +308,14 @@ __global__ __launch_bounds__(kThreads) void quantize_rowtile_kernel(const void* 
   const int64_t groups = (int64_t)gridDim.x * (kThreads / 16);
   for (int64_t tile = (int64_t)blockIdx.x * (kThreads / 16) + (threadIdx.x >> 4); tile < ntiles;
        tile += groups) {
-    // All 16 lanes of a group share `tile`, so the loop trip count is uniform per group;
-    // the shuffles below stay inside the group (xor offsets < 16).
+    // All 16 lanes of a group share `tile`, so the trip count is uniform per
+    // group and the shuffles below (xor offsets < 16) stay inside the group.
     const int64_t r = tile / ntc, tc = tile - r * ntc;
     const int64_t c = tc * 128 + sub * 8;
     const bool valid = c < cols;
     float v[8];
-    if (valid) {
-      load8<XT>(x, r * cols + c, v);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-    }
     uint32_t m = 0u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t a = f2u(v[i]) & 0x7FFFFFFFu;
-      m = m > a ? m : a;
-    }
+    if (valid) load8<XT>(x, r * cols + c, v, m);
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) {
       const uint32_t o = (uint32_t)__shfl_xor((int)m, off, 64);
@@ -233,9 +324,11 @@ __global__ __launch_bounds__(kThreads) void quantize_rowtile_kernel(const void* 
     float s = 1.0f, si = 1.0f;
     scale_from_amax_bits<FMT>(m, &s, &si);
     if (valid) {
-      uint32_t dummy_a = 0u, dummy_c = 0u;
-      const uint2 w = cast8<FMT, false>(v, s, dummy_a, dummy_c);
-      *reinterpret_cast<uint2*>(q + r * cols + c) = w;
+      const bool finite = m <= 0x7F800000u;
+      uint32_t unused = 0u;
+      const uint32_t c0 = scale_encode4<FMT, false>(&v[0], s, finite, unused);
+      const uint32_t c1 = scale_encode4<FMT, false>(&v[4], s, finite, unused);
+      *reinterpret_cast<uint2*>(q + r * cols + c) = make_uint2(c0, c1);
     }
     if (sub == 0) scale_inv[tile] = si;
   }
@@ -247,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void quantize_block128_kernel(const void*
                                                                      int64_t rows, int64_t cols,
                                                                      uint8_t* __restrict__ q,
                                                                      float* __restrict__ scale_inv) {
-  __shared__ uint32_t s_max[kThreads / 64];
+  __shared__ uint32_t s_max[kWaves];
   const int64_t row0 = (int64_t)blockIdx.y * 128, col0 = (int64_t)blockIdx.x * 128;
   const int t = threadIdx.x;
   const int64_t c = col0 + (t & 15) * 8;
@@ -256,32 +349,27 @@ __global__ __launch_bounds__(kThreads) void quantize_block128_kernel(const void*
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t r = row0 + i * 16 + (t >> 4);
-    if (r < rows && c < cols) {
-      load8<XT>(x, r * cols + c, v[i]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t a = f2u(v[i][j]) & 0x7FFFFFFFu;
-      m = m > a ? m : a;
-    }
+    uint32_t vm = 0u;
+    if (r < rows && c < cols) load8<XT>(x, r * cols + c, v[i], vm);
+    m = m > vm ? m : vm;
   }
   m = wave_max_u32(m);
   if ((t & 63) == 0) s_max[t >> 6] = m;
   __syncthreads();
   m = s_max[0];
 #pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) m = m > s_max[w] ? m : s_max[w];
+  for (int w = 1; w < kWaves; ++w) m = m > s_max[w] ? m : s_max[w];
   float s = 1.0f, si = 1.0f;
   scale_from_amax_bits<FMT>(m, &s, &si);
+  const bool finite = m <= 0x7F800000u;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t r = row0 + i * 16 + (t >> 4);
     if (r < rows && c < cols) {
-      uint32_t dummy_a = 0u, dummy_c = 0u;
-      *reinterpret_cast<uint2*>(q + r * cols + c) = cast8<FMT, false>(v[i], s, dummy_a, dummy_c);
+      uint32_t unused = 0u;
+      const uint32_t c0 = scale_encode4<FMT, false>(&v[i][0], s, finite, unused);
+      const uint32_t c1 = scale_encode4<FMT, false>(&v[i][4], s, finite, unused);
+      *reinterpret_cast<uint2*>(q + r * cols + c) = make_uint2(c0, c1);
     }
   }
   if (t == 0) scale_inv[blockIdx.y * gridDim.x + blockIdx.x] = si;
@@ -290,20 +378,15 @@ __global__ __launch_bounds__(kThreads) void quantize_block128_kernel(const void*
 // ---------------------------------------------------------------------------
 // Launch helpers (template dispatch).
 // ---------------------------------------------------------------------------
-int flat_grid(int64_t nchunk) {
-  // Enough workgroups to cover the tensor in at most ~2 trips of the 2-chunk loop,
-  // capped so that small tensors launch few groups.
-  int64_t g = (nchunk + 2 * kThreads - 1) / (2 * kThreads);
-  if (g < 1) g = 1;
-  if (g > 16384) g = 16384;
-  return (int)g;
-}
-
 template <int XT, int FMT, bool WQ, bool SAT>
 void launch_flat_t(const void* x, int64_t n, const float* scale, uint8_t* q, uint32_t* amax_bits,
                    unsigned long long* sat, hipStream_t st) {
-  hipLaunchKernelGGL((quantize_flat_kernel<XT, FMT, WQ, SAT>), dim3(flat_grid(n >> 4)),
-                     dim3(kThreads), 0, st, x, n, scale, q, amax_bits, sat);
+  constexpr int EPV = Vec<XT>::EPV;
+  const int64_t per_block = (int64_t)kThreads * kVecPerLane;
+  int64_t g = (n / EPV + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL((quantize_flat_kernel<XT, FMT, WQ, SAT>), dim3((unsigned)g), dim3(kThreads), 0, st, x, n,
+                     scale, q, amax_bits, sat);
 }
 
 template <int XT, int FMT>

@@ -17,7 +17,7 @@ from fp8_precision_numerics_amd import _binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp8mi.h")
 
-OK, ENULL, ESHAPE, EALIGN, EFMT, EDTYPE, ELAUNCH, EDEV = 0, -1, -2, -3, -4, -5, -6, -7
+OK, ENULL, ESHAPE, EALIGN, EFMT, EDTYPE, ELAUNCH, EDEV, EACCUM = 0, -1, -2, -3, -4, -5, -6, -7, -8
 A16 = ctypes.c_void_p(0x10000)        # 16-B aligned fake address (never dereferenced)
 A8 = ctypes.c_void_p(0x10008)         # misaligned fake address
 
@@ -42,8 +42,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert fm.version() == 100
-    for code in (OK, ENULL, ESHAPE, EALIGN, EFMT, EDTYPE, ELAUNCH, EDEV):
+    assert fm.version() == 200
+    for code in (OK, ENULL, ESHAPE, EALIGN, EFMT, EDTYPE, ELAUNCH, EDEV, EACCUM):
         assert fm.status_string(code) and fm.status_string(code) != "unknown status"
     assert fm.status_string(12345) == "unknown status"
 
@@ -75,17 +75,18 @@ def test_amax_update_argument_errors(lib):
 
 def test_gemm_argument_errors(lib):
     g = lib.fp8_gemm
-    assert g(A16, 3, A16, 0, 16, 16, 16, A16, A16, A16, 0, None) == EFMT
-    assert g(A16, 0, A16, 0, 16, 16, 16, A16, A16, A16, 4, None) == EDTYPE
-    assert g(A16, 0, A16, 0, 16, 16, 0, A16, A16, A16, 0, None) == ESHAPE
-    assert g(A16, 0, A16, 0, -1, 16, 16, A16, A16, A16, 0, None) == ESHAPE
-    assert g(A16, 0, A16, 0, 1 << 31, 16, 16, A16, A16, A16, 0, None) == ESHAPE
-    assert g(A16, 0, A16, 0, 16, 16, 24, A16, A16, A16, 0, None) == EALIGN     # K % 16
-    assert g(None, 0, A16, 0, 16, 16, 16, A16, A16, A16, 0, None) == ENULL
-    assert g(A16, 0, A16, 0, 16, 16, 16, None, A16, A16, 0, None) == ENULL
-    assert g(A8, 0, A16, 0, 16, 16, 16, A16, A16, A16, 0, None) == EALIGN
-    assert g(A16, 0, A16, 0, 16, 16, 16, A16, A16, A8, 0, None) == EALIGN
-    assert g(None, 0, None, 0, 0, 16, 16, None, None, None, 0, None) == OK      # M == 0 is a no-op
+    assert g(A16, 3, A16, 0, 16, 16, 16, A16, A16, A16, 0, 0, None) == EFMT
+    assert g(A16, 0, A16, 0, 16, 16, 16, A16, A16, A16, 4, 0, None) == EDTYPE
+    assert g(A16, 0, A16, 0, 16, 16, 16, A16, A16, A16, 0, 7, None) == EACCUM
+    assert g(A16, 0, A16, 0, 16, 16, 0, A16, A16, A16, 0, 0, None) == ESHAPE
+    assert g(A16, 0, A16, 0, -1, 16, 16, A16, A16, A16, 0, 0, None) == ESHAPE
+    assert g(A16, 0, A16, 0, 1 << 31, 16, 16, A16, A16, A16, 0, 0, None) == ESHAPE
+    assert g(A16, 0, A16, 0, 16, 16, 24, A16, A16, A16, 0, 0, None) == EALIGN     # K % 16
+    assert g(None, 0, A16, 0, 16, 16, 16, A16, A16, A16, 0, 0, None) == ENULL
+    assert g(A16, 0, A16, 0, 16, 16, 16, None, A16, A16, 0, 0, None) == ENULL
+    assert g(A8, 0, A16, 0, 16, 16, 16, A16, A16, A16, 0, 0, None) == EALIGN
+    assert g(A16, 0, A16, 0, 16, 16, 16, A16, A16, A8, 0, 0, None) == EALIGN
+    assert g(None, 0, None, 0, 0, 16, 16, None, None, None, 0, 0, None) == OK      # M == 0 is a no-op
 
 
 def test_blockwise_and_grouped_argument_errors(lib):
@@ -95,16 +96,17 @@ def test_blockwise_and_grouped_argument_errors(lib):
     assert b(A16, 0, 4, 128, 1, 0, None, A16, None) == ENULL
     assert b(A8, 0, 4, 128, 1, 0, A16, A16, None) == EALIGN
     gg = lib.fp8_grouped_gemm
-    assert gg(A16, A16, A16, A16, A16, 0, 16, 16, 128, A16, 0, None) == ESHAPE
-    assert gg(A16, A16, A16, A16, A16, 2000, 16, 16, 128, A16, 0, None) == ESHAPE
-    assert gg(A16, A16, A16, A16, A16, 2, 16, 16, 120, A16, 0, None) == EALIGN
-    assert gg(A16, A16, A16, A16, None, 2, 16, 16, 128, A16, 0, None) == ENULL
-    assert gg(A16, A16, A16, A16, A16, 2, 16, 16, 128, A16, 9, None) == EDTYPE
+    assert gg(A16, A16, A16, A16, A16, 0, 16, 16, 128, A16, 0, 0, None) == ESHAPE
+    assert gg(A16, A16, A16, A16, A16, 2000, 16, 16, 128, A16, 0, 0, None) == ESHAPE
+    assert gg(A16, A16, A16, A16, A16, 2, 16, 16, 120, A16, 0, 0, None) == EALIGN
+    assert gg(A16, A16, A16, A16, None, 2, 16, 16, 128, A16, 0, 0, None) == ENULL
+    assert gg(A16, A16, A16, A16, A16, 2, 16, 16, 128, A16, 9, 0, None) == EDTYPE
+    assert gg(A16, A16, A16, A16, A16, 2, 16, 16, 128, A16, 0, 2, None) == EACCUM
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device path")
 def test_valid_arguments_without_a_device_report_device_error(lib):
-    assert lib.fp8_gemm(A16, 0, A16, 0, 16, 16, 16, A16, A16, A16, 0, None) == EDEV
+    assert lib.fp8_gemm(A16, 0, A16, 0, 16, 16, 16, A16, A16, A16, 0, 0, None) == EDEV
     assert lib.fp8_amax_update(A16, 16, A16, A16, 0, A16, A16, None, None) == EDEV
 
 
