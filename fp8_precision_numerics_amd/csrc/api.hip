@@ -11,6 +11,7 @@
 namespace {
 
 constexpr int64_t kMaxDim = 0x7FFFFFFF;             // kernels index rows/cols with 32-bit ints
+constexpr int64_t kMaxGemmK = int64_t(1) << 23;     // 256 rows x K bytes of a tile slab in a 32-bit buffer offset
 constexpr int64_t kMaxElems = (int64_t)1 << 40;     // sanity bound on any one tensor
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_ok[kMaxDevices];         // 0 unknown, 1 gfx950, -1 not usable
@@ -102,7 +103,7 @@ int fp8_gemm(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t M, int6
   if (!fmt_ok(fa) || !fmt_ok(fb)) return FP8MI_ERR_FORMAT;
   if (!dtype_ok(ctype)) return FP8MI_ERR_DTYPE;
   if (!accum_ok(accum)) return FP8MI_ERR_ACCUM;
-  if (M < 0 || N < 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8MI_ERR_SHAPE;
+  if (M < 0 || N < 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxGemmK) return FP8MI_ERR_SHAPE;
   if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N)) return FP8MI_ERR_SHAPE;
   if ((K & 15) != 0) return FP8MI_ERR_ALIGN;
   if (((M + 127) / 128) * ((N + 127) / 128) > kMaxDim) return FP8MI_ERR_SHAPE;

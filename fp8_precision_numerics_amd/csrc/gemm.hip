@@ -7,12 +7,12 @@
 //
 // Design (gfx950): a workgroup computes a BM x BN output tile with WM x WN
 // wavefronts.  Each 128-deep K step moves a BM x 128 slab of A and a BN x 128
-// slab of B from HBM/L2 straight into one of two LDS buffers
-// (global_load_lds, issued one step ahead, no register staging), while the
-// wavefronts contract the other buffer on the matrix cores (see
+// slab of B from HBM/L2 straight into one of two LDS buffers (buffer loads
+// with the LDS as destination, issued one step ahead, no register staging),
+// while the wavefronts contract the other buffer on the matrix cores (see
 // gemm_tile.hpp for the two accumulation modes).  One barrier per K step.
-// The epilogue multiplies by sinv_a·sinv_b and stores bf16 or fp32 directly
-// from the accumulators.
+// The epilogue multiplies by sinv_a·sinv_b and writes the tile through LDS as
+// whole bf16 or fp32 rows.
 #include "gemm_kernel.hpp"
 #include "launch.hpp"
 
@@ -23,7 +23,7 @@ template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, int MODE>
 hipError_t run(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K,
                const float* sa, const float* sb, void* C, hipStream_t st) {
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-  const int group_m = 8;
+  const int group_m = 16;
   hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, FA, FB, OUT, MODE>),
                      dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * WM * WN), 0, st, A, B, (int)M,
                      (int)N, (int)K, sa, sb, C, tiles_m, tiles_n, group_m);
@@ -33,11 +33,13 @@ hipError_t run(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t
 template <int FA, int FB, int OUT, int MODE>
 hipError_t dispatch_shape(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K,
                           const float* sa, const float* sb, void* C, hipStream_t st) {
-  // The fp16 path holds raw and widened fragments, so it spreads the 256x256
-  // tile over 8 wavefronts (128x64 each); the FP8 path uses 4 (128x128 each).
-  constexpr int WN_BIG = MODE == kAccumExact ? 4 : 2;
-  if (M >= 1024 && N >= 1024)
-    return run<256, 256, 2, WN_BIG, FA, FB, OUT, MODE>(A, B, M, N, K, sa, sb, C, st);
+  // 256x256 tiles.  fp16 path: 4 wavefronts (one per SIMD, 128x128 each, the
+  // accumulators in the AGPR half of the register file).  FP8 path: 8
+  // wavefronts (two per SIMD, 64x128 each) to hide more latency.
+  if (M >= 1024 && N >= 1024) {
+    if constexpr (MODE == kAccumExact) return run<256, 256, 2, 2, FA, FB, OUT, MODE>(A, B, M, N, K, sa, sb, C, st);
+    else return run<256, 256, 4, 2, FA, FB, OUT, MODE>(A, B, M, N, K, sa, sb, C, st);
+  }
   return run<128, 128, 2, 2, FA, FB, OUT, MODE>(A, B, M, N, K, sa, sb, C, st);
 }
 

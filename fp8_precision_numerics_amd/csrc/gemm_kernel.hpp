@@ -2,13 +2,22 @@
 // the host-side dispatch).
 //
 // Main loop of one workgroup, per 128-deep K step t (stage = t % 2):
-//   * the direct-to-LDS loads of step t+1 into the other stage are issued
-//     spread through the MFMA stream of step t (scheduling hints below);
-//   * the wave's B fragments for step t are already in registers; its A
-//     fragments are read one 16-row block ahead (af[(i+1)&1] while the MFMAs of
-//     block i run), so LDS latency hides behind matrix-core time;
+//   * the direct-to-LDS loads of step t+1 into the other stage are issued at
+//     the start of step t and only waited for at the end of the step, so
+//     their latency overlaps the whole step;
+//   * FP8 path: the wave's A fragments for step t are in registers; its B
+//     fragments are read one 16-row block ahead (bf[(j+1)&1] while the MFMAs
+//     of block j run).  fp16 path: all raw FP8 fragments of the step are in
+//     registers and widened to fp16 per 16-deep sub-step;
 //   * at the end of the step: wait for this lane's loads, barrier, then read
-//     the B fragments and the first A fragment of step t+1.
+//     the fragments of step t+1.
+//
+// Operand slabs are fetched with buffer loads: one buffer resource per tile
+// covers the rows [tile start, M) (or N) of the operand, so rows past the
+// edge fall outside the resource and never touch memory; they only feed
+// output rows or columns that are not stored.  The per-lane offset is the same
+// for every load of a step (the row group and K offset are scalar), which keeps
+// the address state to a single register.
 #pragma once
 
 #include "gemm_tile.hpp"
@@ -17,8 +26,124 @@ namespace fp8mi {
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;
-constexpr int kSchedVmemRead = 0x020;
 constexpr int kSchedDsRead = 0x100;
+
+// dword 3 of a raw (untyped, stride 0) buffer resource on gfx9: 32-bit data format.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const uint8_t* base, int64_t rows_left, int64_t ld) {
+  int64_t bytes = rows_left * ld;
+  bytes = bytes < 0xFFFFFFFFll ? bytes : 0xFFFFFFFFll;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)(uint32_t)bytes, kBufferRsrcWord3);
+}
+
+// The K loop shared by both accumulation modes.  `step` handles one full step
+// whose successor is also full: load step kt+1 into `nxt` while contracting
+// `cur`.  The two stage pointers are restrict-qualified so that, once inlined,
+// the compiler knows the direct-to-LDS writes into `nxt` cannot alias the
+// fragment reads from `cur` and does not wait for the loads before those reads
+// (it would otherwise serialise load and compute).  Two steps per iteration
+// keep each stage pointer fixed at compile time.
+template <class Issue, class Ragged, class Frags, class Compute, class Hint>
+__device__ __forceinline__ void run_main_loop(uint8_t* s0, uint8_t* s1, int nfull, int nk, bool ragged_k,
+                                              Issue& issue_direct, Ragged& stage_ragged, Frags& load_frags,
+                                              Compute& compute, Hint& interleave) {
+  auto step = [&](uint8_t* __restrict__ nxt, const uint8_t* __restrict__ cur, int kt_next) {
+    issue_direct(nxt, kt_next);
+    // Keep the loads at the head of the step and the MFMAs inside it: left
+    // alone, the scheduler may sink the loads below the MFMAs or the MFMAs
+    // below the barrier, either of which leaves the loads no time to land.
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmem();
+    __syncthreads();
+    load_frags(nxt);
+  };
+  if (nfull > 0) issue_direct(s0, 0); else stage_ragged(0, 0);
+  wait_vmem();
+  __syncthreads();
+  load_frags(s0);
+  int kt = 0;
+  for (; kt + 2 < nfull; kt += 2) {
+    step(s1, s0, kt + 1);
+    step(s0, s1, kt + 2);
+  }
+  if (kt + 1 < nfull) {
+    step(s1, s0, kt + 1);
+    ++kt;
+  }
+  // Last full step (its successor, if any, is the ragged step), then the ragged step.
+  if (kt < nfull) {
+    uint8_t* cur = (kt & 1) ? s1 : s0;
+    uint8_t* nxt = (kt & 1) ? s0 : s1;
+    if (ragged_k) stage_ragged(kt + 1, (kt & 1) ^ 1);
+    compute(cur);
+    ++kt;
+    if (ragged_k) {
+      wait_vmem();
+      __syncthreads();
+      load_frags(nxt);
+    }
+  }
+  if (kt < nk) compute((kt & 1) ? s1 : s0);
+}
+
+// Epilogue: the scaled output tile goes through LDS (free once the K loop is
+// done) so that global stores are whole contiguous rows: each lane stores 16
+// bytes, consecutive lanes consecutive addresses.  Storing straight from the
+// matrix-core layout writes 8-16 byte pieces of many rows per instruction,
+// which costs several times the output's size in memory traffic.  Tile rows
+// are BN*sizeof(out) bytes; the 16-byte granule q of row r sits at position
+// q ^ (r mod min(granules per row, 32)).  A tile that does not fit the LDS goes
+// out in row passes.
+template <int OUT, int BM, int BN, int NT>
+struct TileWriter {
+  static constexpr int CB = OUT == kF32 ? 4 : 2;           // bytes per output element
+  static constexpr int ROWB = BN * CB;                     // bytes per tile row
+  static constexpr int GR = ROWB / 16;                     // granules per row
+  static constexpr int SWZ = (GR < 32 ? GR : 32) - 1;
+  static_assert(GR >= 8 && (GR & (GR - 1)) == 0, "tile row must be a power-of-two number of granules");
+  uint8_t* lds;
+  int pass_rows;
+  __device__ __forceinline__ int pos(int r, int byte) const {
+    return r * ROWB + ((((byte >> 4) ^ (r & SWZ)) & (GR - 1)) << 4) + (byte & 15);
+  }
+  // Four consecutive outputs (n_local multiple of 4) of tile row r_local, already scaled.
+  __device__ __forceinline__ void put(int r_local, int n_local, const v4f& v) const {
+    uint8_t* p = lds + pos(r_local, n_local * CB);
+    if constexpr (OUT == kF32) {
+      *reinterpret_cast<v4f*>(p) = v;
+    } else {
+      const v2bf lo = __builtin_convertvector((v2f){v[0], v[1]}, v2bf);
+      const v2bf hi = __builtin_convertvector((v2f){v[2], v[3]}, v2bf);
+      *reinterpret_cast<uint2*>(p) = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+    }
+  }
+  // Copy rows [0, pass_rows) of the staged pass to C rows m0.. (all threads).
+  __device__ __forceinline__ void flush(void* C, int64_t M, int64_t N, int64_t m0, int64_t n0, int t) const {
+    const bool full_cols = n0 + BN <= N && ((N * CB) & 15) == 0;
+    for (int idx = t; idx < pass_rows * GR; idx += NT) {
+      const int r = idx / GR, q = idx % GR;
+      const int64_t m = m0 + r;
+      if (m >= M) break;  // rows are visited in order
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + pos(r, q * 16));
+      uint8_t* dst = reinterpret_cast<uint8_t*>(C) + (m * N + n0) * CB + q * 16;
+      if (full_cols) {
+        *reinterpret_cast<uint4*>(dst) = v;
+      } else {
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(&v);
+        const int64_t nq = n0 + q * (16 / CB);
+        for (int e = 0; e < 16 / CB; ++e)
+          if (nq + e < N) {
+            if constexpr (OUT == kF32) reinterpret_cast<float*>(dst)[e] = reinterpret_cast<const float*>(src)[e];
+            else reinterpret_cast<uint16_t*>(dst)[e] = reinterpret_cast<const uint16_t*>(src)[e];
+          }
+      }
+    }
+  }
+};
 
 template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, int MODE>
 __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
@@ -27,9 +152,13 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
     int tiles_m, int tiles_n, int group_m) {
   constexpr int NW = WM * WN, NT = 64 * NW;
   constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int FM = WTM / 16, FN = WTN / 16;
+  // Output block of one matrix-core instruction: 16x16 (FP8 path), 32x32 (fp16 path).
+  constexpr int BLK = MODE == kAccumMfma8 ? 16 : 32;
+  constexpr int FM = WTM / BLK, FN = WTN / BLK;
   constexpr int LQA = BM / 8 / NW, LQB = BN / 8 / NW;  // direct-load instructions per wave per step
-  static_assert(FM >= 2 && FN >= 1 && BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile shape");
+  static_assert(FM >= 1 && FN >= 1 && WTM % BLK == 0 && WTN % BLK == 0, "wave tile shape");
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows must split evenly over the wavefronts");
+  static_assert(NW % 2 == 0, "the swizzle of a lane's load must not depend on its row group");
   constexpr int STAGE = (BM + BN) * kBK;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
@@ -42,33 +171,24 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
   const int nk = (K + kBK - 1) / kBK;
   const bool ragged_k = (K % kBK) != 0;
 
-  // Per-lane source pointers of the direct loads (row clamped at the edge; the
-  // granule index g is this lane's swizzled 16-B column of its row).
-  const int r_in = lane >> 3, g = (lane & 7) ^ r_in;
-  const uint8_t* pa[LQA];
-  const uint8_t* pb[LQB];
-#pragma unroll
-  for (int q = 0; q < LQA; ++q) {
-    int64_t r = m_base + (w + q * NW) * 8 + r_in;
-    r = r < M ? r : M - 1;
-    pa[q] = A + r * K + g * 16;
-  }
-#pragma unroll
-  for (int q = 0; q < LQB; ++q) {
-    int64_t r = n_base + (w + q * NW) * 8 + r_in;
-    r = r < N ? r : N - 1;
-    pb[q] = B + r * K + g * 16;
-  }
-  auto issue_direct = [&](int kt, int stage) {
-    uint8_t* sa = smem + stage * STAGE;
-    uint8_t* sb = sa + BM * kBK;
+  // Direct loads: load q of wave w fills tile rows (w + q*NW)*8 .. +7; lane i
+  // fills position i & 7 of row i >> 3 of that group with the granule stored
+  // there under the swizzle (which depends on the row's low 4 bits only, i.e.
+  // not on q since NW is even).
+  const __amdgpu_buffer_rsrc_t ra = operand_rsrc(A + m_base * K, M - m_base, K);
+  const __amdgpu_buffer_rsrc_t rb = operand_rsrc(B + n_base * K, N - n_base, K);
+  const int lrow = w * 8 + (lane >> 3);
+  const int voff = lrow * K + (((lane & 7) ^ lds_swz(lrow)) & 7) * 16;
+  auto issue_direct = [&](uint8_t* dst, int kt) {
     const int k0 = kt * kBK;
 #pragma unroll
     for (int q = 0; q < LQA; ++q)
-      __builtin_amdgcn_global_load_lds((global_void_t*)(pa[q] + k0), (lds_void_t*)(sa + (w + q * NW) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(dst + (w + q * NW) * 1024), 16, voff,
+                                               q * NW * 8 * K + k0, 0, 0);
 #pragma unroll
     for (int q = 0; q < LQB; ++q)
-      __builtin_amdgcn_global_load_lds((global_void_t*)(pb[q] + k0), (lds_void_t*)(sb + (w + q * NW) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(dst + BM * kBK + (w + q * NW) * 1024), 16, voff,
+                                               q * NW * 8 * K + k0, 0, 0);
   };
   // Zero-filled register path for a ragged last K step.
   auto stage_ragged = [&](int kt, int stage) {
@@ -77,111 +197,142 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
     tile_load_zero_fill<BN, NT>(B, K, n_base, N, kt * kBK, K, sa + BM * kBK, t);
   };
 
-  v4f acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  // Fragment reads.  FP8 path (16x16x128): lane l takes row l & 15 of a
+  // 16-row block and the 32-byte K slice l >> 4 (granules 2h, 2h+1).  fp16
+  // path (32x32x16, eight K sub-steps of 16): lane l takes row l & 31 of a
+  // 32-row block and the 64-byte half l >> 5 of the K step (granules 4h..4h+3);
+  // sub-step s uses bytes [8s, 8s+8) of it, for both operands alike.  Block
+  // starts are multiples of 16 rows, so the swizzle of a lane's row is fixed.
+  const int rr = lane & (BLK - 1), hh = lane / BLK;
+  const int swz = lds_swz(rr);
+  auto granule = [&](const uint8_t* tile, int row0, int g) {
+    return *reinterpret_cast<const uint4*>(tile + (row0 + rr) * kBK + (((g ^ swz) & 7) << 4));
+  };
 
-  const int a_row = wm * WTM + (lane & 15), b_row = wn * WTN + (lane & 15);
-  v8i bf[FN], af[2];
+  uint8_t* const s0 = smem;
+  uint8_t* const s1 = smem + STAGE;
+  const int nfull = K / kBK;
 
-  // Contract the stage at `sa` (B fragments and the first A fragment already in registers).
-  auto compute = [&](const uint8_t* sa) {
-    if constexpr (MODE == kAccumMfma8) {
+  // Stage the output tile through LDS in passes of as many rows as fit;
+  // `emit(r_lo, r_hi, writer)` puts this lane's outputs of rows [r_lo, r_hi).
+  auto write_tile = [&](auto&& emit) {
+    using TW = TileWriter<OUT, BM, BN, NT>;
+    constexpr int PASS = (2 * STAGE / TW::ROWB) < BM ? (2 * STAGE / TW::ROWB) : BM;
+    static_assert(BM % PASS == 0, "output passes must tile the rows");
+    TW tw{smem, PASS};
+#pragma unroll 1
+    for (int r0 = 0; r0 < BM; r0 += PASS) {
+      __syncthreads();  // the LDS is free: K loop or previous pass done
+      emit(r0, r0 + PASS, tw);
+      __syncthreads();
+      tw.flush(C, M, N, m_base + r0, n_base, t);
+    }
+  };
+
+  if constexpr (MODE == kAccumMfma8) {
+    v4f acc[FM][FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        if (i + 1 < FM) af[(i + 1) & 1] = lds_frag(sa, a_row + (i + 1) * 16, lane);
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma_fp8<FB, FA>(bf[j], af[i & 1], acc[i][j]);
+      for (int j = 0; j < FN; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    auto frag = [&](const uint8_t* tile, int row0) {
+      const uint4 lo = granule(tile, row0, 2 * hh), hi = granule(tile, row0, 2 * hh + 1);
+      return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+    // A fragments of the step stay in registers; B fragments stream one
+    // 16-row block ahead (bf[(j+1)&1] is read while the MFMAs of block j run).
+    v8i af[FM], bf[2];
+    auto load_frags = [&](const uint8_t* st) {
+      bf[0] = frag(st + BM * kBK, wn * WTN);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = frag(st, wm * WTM + i * 16);
+    };
+    // Contract the stage at `st` (A fragments and the first B fragment already in registers).
+    auto compute = [&](const uint8_t* st) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        if (j + 1 < FN) bf[(j + 1) & 1] = frag(st + BM * kBK, wn * WTN + (j + 1) * 16);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) acc[i][j] = mfma_fp8<FB, FA>(bf[j & 1], af[i], acc[i][j]);
       }
-    } else {
-      v8h bh[4][FN];
+    };
+    // Scheduling hint: per B block, its two LDS reads ahead of its MFMAs.
+    auto interleave = [&]() {
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) bh[s][j] = widen8<FB>((uint32_t)bf[j][2 * s], (uint32_t)bf[j][2 * s + 1]);
+      for (int j = 0; j < FN; ++j) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, FM, 0);
+      }
+    };
+    run_main_loop(s0, s1, nfull, nk, ragged_k, issue_direct, stage_ragged, load_frags, compute, interleave);
+
+    // Lane l holds row m = l & 15 of each 16x16 block (the A operand went
+    // second) and columns n = 4(l >> 4) .. +3.
+    const float sc = sinv_a[0] * sinv_b[0];
+    write_tile([&](int r_lo, int r_hi, auto& tw) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        if (i + 1 < FM) af[(i + 1) & 1] = lds_frag(sa, a_row + (i + 1) * 16, lane);
+        const int r = wm * WTM + i * 16 + (lane & 15);
+        if (r < r_lo || r >= r_hi) continue;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const v8h ah = widen8<FA>((uint32_t)af[i & 1][2 * s], (uint32_t)af[i & 1][2 * s + 1]);
+        for (int j = 0; j < FN; ++j) tw.put(r - r_lo, wn * WTN + j * 16 + 4 * (lane >> 4), acc[i][j] * sc);
+      }
+    });
+  } else {
+    v16f acc[FM][FN];
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bh[s][j], ah, acc[i][j], 0, 0, 0);
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = (v16f){};
+    // Raw FP8 fragments of the whole step: 4 granules (64 bytes) per block.
+    uint4 ar[FM][4], br[FN][4];
+    auto load_frags = [&](const uint8_t* st) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) br[j][c] = granule(st + BM * kBK, wn * WTN + j * 32, 4 * hh + c);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) ar[i][c] = granule(st, wm * WTM + i * 32, 4 * hh + c);
+      }
+    };
+    auto compute = [&](const uint8_t*) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        v8h bh[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const uint4 g = br[j][s >> 1];
+          bh[j] = (s & 1) ? widen8<FB>(g.z, g.w) : widen8<FB>(g.x, g.y);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const uint4 g = ar[i][s >> 1];
+          const v8h ah = (s & 1) ? widen8<FA>(g.z, g.w) : widen8<FA>(g.x, g.y);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bh[j], ah, acc[i][j], 0, 0, 0);
         }
       }
-    }
-  };
-  // Interleave hint for a step whose next-stage direct loads are in the same
-  // block: per A block, its 2 LDS reads, half its MFMAs, a share of the loads,
-  // the other half.
-  auto interleave = [&]() {
-    if constexpr (MODE == kAccumMfma8) {
+    };
+    auto interleave = [&]() {};
+    run_main_loop(s0, s1, nfull, nk, ragged_k, issue_direct, stage_ragged, load_frags, compute, interleave);
+
+    // Lane l holds row m = l & 31 of each 32x32 block (the A operand went
+    // second) and columns n = 8g + 4(l >> 5) + 0..3 in registers 4g..4g+3.
+    const float sc = sinv_a[0] * sinv_b[0];
+    write_tile([&](int r_lo, int r_hi, auto& tw) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, FN / 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, (LQA + LQB + FM - 1) / FM, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, FN - FN / 2, 0);
+        const int r = wm * WTM + i * 32 + (lane & 31);
+        if (r < r_lo || r >= r_hi) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const v4f v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+            tw.put(r - r_lo, wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5), v * sc);
+          }
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * FN, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, (LQA + LQB + FM - 1) / FM, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * FN, 0);
-      }
-    }
-  };
-  auto load_frags = [&](const uint8_t* sa) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) bf[j] = lds_frag(sa + BM * kBK, b_row + j * 16, lane);
-    af[0] = lds_frag(sa, a_row, lane);
-  };
-
-  const int nfull = K / kBK;
-  if (nfull > 0) issue_direct(0, 0); else stage_ragged(0, 0);
-  wait_vmem();
-  __syncthreads();
-  load_frags(smem);
-  // Full steps whose successor is also full: loads unconditional, interleaved.
-  int kt = 0;
-  for (; kt + 1 < nfull; ++kt) {
-    const int cur = kt & 1;
-    issue_direct(kt + 1, cur ^ 1);
-    compute(smem + cur * STAGE);
-    interleave();
-    wait_vmem();
-    __syncthreads();
-    load_frags(smem + (cur ^ 1) * STAGE);
-  }
-  // Last full step (its successor, if any, is the ragged step), then the ragged step.
-  if (kt < nfull) {
-    const int cur = kt & 1;
-    if (ragged_k) stage_ragged(kt + 1, cur ^ 1);
-    compute(smem + cur * STAGE);
-    ++kt;
-    if (ragged_k) {
-      wait_vmem();
-      __syncthreads();
-      load_frags(smem + (cur ^ 1) * STAGE);
-    }
-  }
-  if (kt < nk) compute(smem + (kt & 1) * STAGE);
-
-  const float sc = sinv_a[0] * sinv_b[0];
-  const bool vec_ok = (N & 3) == 0;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int64_t m = m_base + wm * WTM + i * 16 + (lane & 15);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t n = n_base + wn * WTN + j * 16 + 4 * (lane >> 4);
-      store4<OUT>(C, N, m, n, M, acc[i][j] * sc, vec_ok);
-    }
+    });
   }
 }
 

@@ -27,10 +27,15 @@
 // any assignment of K values to (lane, register) slots works as long as both
 // operands use the same one.
 //
-// Operand tiles live in LDS as rows of 128 bytes (one K step).  The 16-byte
-// granule g of row r is stored at granule position g ^ (r & 7): the 16-B
-// reads of a fragment (rows r..r+15, same granule) and the loads of eight
-// rows per wave instruction both spread over all granule positions.
+// Operand tiles live in LDS as rows of 128 bytes (one K step); the 16-byte
+// granule g of row r sits at position g ^ swz(r) with
+// swz(r) = (r & 6) | ((r >> 3) & 1).  A fragment read (16 lanes on 16
+// consecutive rows, same granule; lanes 16..63 at granules +2, +4, +6) runs at
+// full LDS rate under this map.  The map was chosen by timing ds_read_b128 on
+// MI355X over every GF(2)-linear map from the row's low four bits to the
+// position: the plain g ^ (r & 7) and g ^ ((r >> 1) & 7) maps run at half
+// rate, an unswizzled tile at a quarter.  The direct-to-LDS loads write 1 KiB
+// contiguous per wave instruction, which the swizzle does not affect.
 #pragma once
 
 #include "device_common.hpp"
@@ -45,7 +50,8 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void global_void_t;
 
-__device__ __forceinline__ int lds_granule(int row, int g) { return row * kBK + (((g ^ row) & 7) << 4); }
+__device__ __forceinline__ int lds_swz(int row) { return (row & 6) | ((row >> 3) & 1); }
+__device__ __forceinline__ int lds_granule(int row, int g) { return row * kBK + (((g ^ lds_swz(row)) & 7) << 4); }
 
 template <int FA, int FB>
 __device__ __forceinline__ v4f mfma_fp8(const v8i& first, const v8i& second, const v4f& c) {
@@ -85,9 +91,10 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int lane) 
 // Move ROWS x 128 bytes (rows row0.. of a row-major byte matrix with row
 // stride ld, column offset k0) into an LDS tile with direct-to-LDS loads: one
 // wave instruction fills 8 rows (1 KiB; lane i writes bytes [16i, 16i+16) of
-// it), so lane i fetches granule (i & 7) ^ (i >> 3) of row i >> 3.  Rows past
-// `rows_valid` are clamped to the last valid row: they only feed output rows
-// or columns that are never stored.  The caller waits for vmcnt before use.
+// it), so lane i fetches the granule that belongs at position i & 7 of row
+// i >> 3 of that group.  Rows past `rows_valid` are clamped to the last valid
+// row: they only feed output rows or columns that are never stored.  The
+// caller waits for vmcnt before use.
 template <int ROWS, int NW>
 __device__ __forceinline__ void tile_load_direct(const uint8_t* __restrict__ base, int64_t ld,
                                                  int64_t row0, int64_t rows_valid, int k0,
@@ -95,10 +102,10 @@ __device__ __forceinline__ void tile_load_direct(const uint8_t* __restrict__ bas
   constexpr int GROUPS = ROWS / 8;
   static_assert(GROUPS % NW == 0, "tile rows must split evenly over the wavefronts");
   const int r_in = lane >> 3;
-  const int g = (lane & 7) ^ r_in;
 #pragma unroll
   for (int q = 0; q < GROUPS / NW; ++q) {
     const int grp = wave + q * NW;
+    const int g = ((lane & 7) ^ lds_swz(grp * 8 + r_in)) & 7;
     int64_t r = row0 + grp * 8 + r_in;
     r = r < rows_valid ? r : rows_valid - 1;
     const uint8_t* src = base + r * ld + k0 + g * 16;

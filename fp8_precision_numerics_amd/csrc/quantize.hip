@@ -129,7 +129,6 @@ __global__ __launch_bounds__(kThreads) void quantize_flat_kernel(
   const bool regular = scale_is_regular(s);
   const int64_t nvec = n / EPV;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t wave_base = ((int64_t)blockIdx.x * kWaves + wave) * (64 * U);
   uint32_t amx = 0u, wcnt = 0u;
   float v[U][EPV];
   uint32_t vm[U];
@@ -146,28 +145,34 @@ __global__ __launch_bounds__(kThreads) void quantize_flat_kernel(
       }
     }
   };
-  if (wave_base + U * 64 <= nvec) {
-    // Whole wave in range (all but the last wave): every load issued before any use.
+  // Grid-stride over wave chunks of 64*U vectors: a persistent grid of a few
+  // workgroups per CU keeps the number of cross-workgroup atomics small.
+  const int64_t wave_stride = (int64_t)gridDim.x * kWaves * (64 * U);
+  for (int64_t wave_base = ((int64_t)blockIdx.x * kWaves + wave) * (64 * U); wave_base < nvec;
+       wave_base += wave_stride) {
+    if (wave_base + U * 64 <= nvec) {
+      // Whole chunk in range: every load issued before any use.
 #pragma unroll
-    for (int u = 0; u < U; ++u) load_vec<XT>(x, wave_base + u * 64 + lane, v[u], vm[u]);
+      for (int u = 0; u < U; ++u) load_vec<XT>(x, wave_base + u * 64 + lane, v[u], vm[u]);
 #pragma unroll
-    for (int u = 0; u < U; ++u) cast_store(u, wave_base + u * 64 + lane);
-  } else {
+      for (int u = 0; u < U; ++u) cast_store(u, wave_base + u * 64 + lane);
+    } else {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t vi = wave_base + u * 64 + lane;
-      vm[u] = 0u;
-      if (vi < nvec) load_vec<XT>(x, vi, v[u], vm[u]);
-    }
+      for (int u = 0; u < U; ++u) {
+        const int64_t vi = wave_base + u * 64 + lane;
+        vm[u] = 0u;
+        if (vi < nvec) load_vec<XT>(x, vi, v[u], vm[u]);
+      }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t vi = wave_base + u * 64 + lane;
-      if (vi < nvec) cast_store(u, vi);
+      for (int u = 0; u < U; ++u) {
+        const int64_t vi = wave_base + u * 64 + lane;
+        if (vi < nvec) cast_store(u, vi);
+      }
     }
   }
-  // Ragged tail (n % EPV elements), element by element, in the last workgroup.
+  // Ragged tail (n % EPV elements), element by element, in workgroup 0.
   const int rem = (int)(n - nvec * EPV);
-  if (blockIdx.x == gridDim.x - 1 && (int)threadIdx.x < rem) {
+  if (blockIdx.x == 0 && (int)threadIdx.x < rem) {
     const int64_t i = nvec * EPV + threadIdx.x;
     const float xv = load1<XT>(x, i);
     const uint32_t m = f2u(xv) & 0x7FFFFFFFu;
@@ -217,11 +222,14 @@ __global__ __launch_bounds__(kThreads) void quantize_transpose_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTile * kPitch];
   const float s = *scale;
   const bool regular = scale_is_regular(s);
-  const int64_t row0 = (int64_t)blockIdx.y * kTile, col0 = (int64_t)blockIdx.x * kTile;
   const int t = threadIdx.x;
   const int vi = t % VPR, rr0 = t / VPR;
   const int64_t vecs_per_row = cols / EPV;
+  const int64_t tiles_c = (cols + kTile - 1) / kTile, tiles = tiles_c * ((rows + kTile - 1) / kTile);
   uint32_t amx = 0u, wcnt = 0u;
+  // Persistent grid: each workgroup walks tiles blockIdx.x, +gridDim.x, ...
+  for (int64_t tile_id = blockIdx.x; tile_id < tiles; tile_id += gridDim.x) {
+  const int64_t row0 = (tile_id / tiles_c) * kTile, col0 = (tile_id % tiles_c) * kTile;
   float v[PASSES][EPV];
   uint32_t vm[PASSES];
   auto cast_pass = [&](int i) {
@@ -276,6 +284,8 @@ __global__ __launch_bounds__(kThreads) void quantize_transpose_kernel(
       for (int k = 0; k < 4; ++k)
         *reinterpret_cast<uint4*>(q_t + (c + k) * rows + r) = make_uint4(o[0][k], o[1][k], o[2][k], o[3][k]);
     }
+  }
+  __syncthreads();  // the LDS tile is rewritten by the next iteration
   }
   block_finish(amx, wcnt, amax_bits, sat);
 }
@@ -378,12 +388,30 @@ __global__ __launch_bounds__(kThreads) void quantize_block128_kernel(const void*
 // ---------------------------------------------------------------------------
 // Launch helpers (template dispatch).
 // ---------------------------------------------------------------------------
+// Workgroups of a persistent cast grid: two per compute unit.  Each workgroup
+// ends with one device-scope atomicMax on the single amax word; those are
+// serialised across the chip (about 10 ns each on MI355X), so the grid is kept
+// near the number of CUs rather than one workgroup per chunk.
+int persistent_groups() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cached[dev] = 2 * cus;
+  }
+  return cached[dev];
+}
+
 template <int XT, int FMT, bool WQ, bool SAT>
 void launch_flat_t(const void* x, int64_t n, const float* scale, uint8_t* q, uint32_t* amax_bits,
                    unsigned long long* sat, hipStream_t st) {
   constexpr int EPV = Vec<XT>::EPV;
   const int64_t per_block = (int64_t)kThreads * kVecPerLane;
   int64_t g = (n / EPV + per_block - 1) / per_block;
+  if (g > persistent_groups()) g = persistent_groups();
   if (g < 1) g = 1;
   hipLaunchKernelGGL((quantize_flat_kernel<XT, FMT, WQ, SAT>), dim3((unsigned)g), dim3(kThreads), 0, st, x, n,
                      scale, q, amax_bits, sat);
@@ -402,7 +430,8 @@ template <int XT, int FMT>
 void launch_transpose_f(const void* x, int64_t rows, int64_t cols, const float* scale, uint8_t* q,
                         uint8_t* q_t, uint32_t* amax_bits, unsigned long long* sat,
                         hipStream_t st) {
-  const dim3 grid((unsigned)((cols + kTile - 1) / kTile), (unsigned)((rows + kTile - 1) / kTile));
+  int64_t tiles = ((cols + kTile - 1) / kTile) * ((rows + kTile - 1) / kTile);
+  const dim3 grid((unsigned)(tiles < persistent_groups() ? tiles : persistent_groups()));
   if (q && sat)
     hipLaunchKernelGGL((quantize_transpose_kernel<XT, FMT, true, true>), grid, dim3(kThreads), 0, st,
                        x, rows, cols, scale, q, q_t, amax_bits, sat);

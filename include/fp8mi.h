@@ -153,7 +153,8 @@ FP8MI_API int fp8_amax_update(float* history, int32_t history_len, int32_t* head
  * accum   fp8mi_accum: FP8MI_ACCUM_EXACT (the FP32-accumulation contract above
  *         for every input) or FP8MI_ACCUM_MFMA_FP8 (native FP8 matrix cores; see
  *         the fp8mi_accum note for its arithmetic).
- * K must be a multiple of 16 (and > 0); M, N >= 0 (M or N == 0 is a no-op).
+ * K must be a multiple of 16, 0 < K <= 2^23 (else FP8MI_ERR_ALIGN / _SHAPE);
+ * M, N >= 0 (M or N == 0 is a no-op).
  * The order in which fp32 partial sums are added is not fixed.
  */
 FP8MI_API int fp8_gemm(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t M, int64_t N, int64_t K,

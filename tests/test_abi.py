@@ -81,6 +81,7 @@ def test_gemm_argument_errors(lib):
     assert g(A16, 0, A16, 0, 16, 16, 0, A16, A16, A16, 0, 0, None) == ESHAPE
     assert g(A16, 0, A16, 0, -1, 16, 16, A16, A16, A16, 0, 0, None) == ESHAPE
     assert g(A16, 0, A16, 0, 1 << 31, 16, 16, A16, A16, A16, 0, 0, None) == ESHAPE
+    assert g(A16, 0, A16, 0, 16, 16, (1 << 23) + 16, A16, A16, A16, 0, 0, None) == ESHAPE   # K limit
     assert g(A16, 0, A16, 0, 16, 16, 24, A16, A16, A16, 0, 0, None) == EALIGN     # K % 16
     assert g(None, 0, A16, 0, 16, 16, 16, A16, A16, A16, 0, 0, None) == ENULL
     assert g(A16, 0, A16, 0, 16, 16, 16, None, A16, A16, 0, 0, None) == ENULL
