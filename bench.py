@@ -37,6 +37,28 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 # Matrix-core peak of the instruction each accumulation mode runs on.
 PEAK_BY_ACCUM = {"exact": PEAK_FP16_TFLOPS, "mfma_fp8": PEAK_FP8_TFLOPS}
 
+# HBM traffic per launch of the FC1 GEMM from two counter runs (FETCH_SIZE, WRITE_SIZE), each scaled by what
+# the same counter reads for a 256 MiB device copy (profiles/gemm_fc1_8192x16384x4096_hbm_traffic.md).  Valid
+# only for the kernel sources they were taken on: GEMM_SOURCES hashed in order must give GEMM_TRAFFIC_SHA256.
+GEMM_SOURCES = ("gemm.hip", "gemm_kernel.hpp", "gemm_tile.hpp", "device_common.hpp")
+GEMM_TRAFFIC_SHA256 = "543aac339ddc11d66faf31ec668a3ca298a60e407bd036ec6538616305e7fcaa"
+GEMM_TRAFFIC = {"exact": {"read_bytes": 1209175402, "write_bytes": 268784384},
+                "mfma_fp8": {"read_bytes": 1209767013, "write_bytes": 271504832}}
+
+
+def gemm_traffic(accum):
+    """Counter-measured HBM bytes per launch, or None once the GEMM sources differ from the measured ones."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "fp8_precision_numerics_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != GEMM_TRAFFIC_SHA256:
+        return None
+    t = GEMM_TRAFFIC[accum]
+    return t["read_bytes"] + t["write_bytes"]
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -52,6 +74,9 @@ def parse():
     p.add_argument("--stream-dtype", default="bf16", choices=["bf16", "f32"])
     p.add_argument("--accum", default="exact", choices=["exact", "mfma_fp8"],
                    help="GEMM accumulation mode of the timed step (the other mode is timed as an extra)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 256 MiB device-to-device copy (3 times): the known-size reference "
+                        "for scaling the HBM traffic counters of a profiler run")
     return p.parse_args()
 
 
@@ -354,6 +379,14 @@ def main():
         sys.exit(1)
     head = headline(torch, fm, args)
     extra = {"headline": head}
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        extra["copy_calibration_bytes"] = src.numel()
+        del src, dst
     if not args.quick:
         extra["stream"] = stream_bench(torch, fm, args.stream_dtype)
         extra["dgrad"] = dgrad_bench(torch, fm)
@@ -381,7 +414,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(head["gemm_tflops"], 1),
                      "peak": PEAK_BY_ACCUM[args.accum], "unit": "TFLOP/s",
                      "frac": round(head["gemm_tflops"] / PEAK_BY_ACCUM[args.accum], 4),
-                     "traffic": None,
+                     "traffic": gemm_traffic(args.accum),
                      "kernel": "gemm_kernel (%s accumulation: %s matrix cores)"
                                % (args.accum, "fp16" if args.accum == "exact" else "fp8")},
         "cpu_baseline": cpu,
