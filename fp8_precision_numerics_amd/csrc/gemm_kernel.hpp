@@ -37,33 +37,63 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const uint8_t* ba
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)(uint32_t)bytes, kBufferRsrcWord3);
 }
 
+// Buffer loads with the LDS as destination, written as inline assembly so that
+// the compiler does not track them: it cannot tell the stages apart and would
+// otherwise wait for every such load before any later LDS read it cannot prove
+// disjoint, i.e. right after issuing them.  The kernel waits for them itself (vmcnt) before the
+// barrier that publishes a stage.  Lane i writes `bytes` at LDS address
+// lds + i*bytes; M0 carries the LDS base (one wait state after it is written).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
+}
+__device__ __forceinline__ void dma_lds16(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff, int soff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(lds)
+               : "memory");
+}
+
+// The next stage's loads are issued in this many groups within a step.
+constexpr int kDmaGroups = 4;
+
 // The K loop shared by both accumulation modes.  `step` handles one full step
 // whose successor is also full: load step kt+1 into `nxt` while contracting
-// `cur`.  The two stage pointers are restrict-qualified so that, once inlined,
-// the compiler knows the direct-to-LDS writes into `nxt` cannot alias the
-// fragment reads from `cur` and does not wait for the loads before those reads
-// (it would otherwise serialise load and compute).  Two steps per iteration
-// keep each stage pointer fixed at compile time.
+// `cur`.  Two steps per iteration keep each stage pointer fixed at compile
+// time.
+//
+// The end of a step waits for this wave's loads and LDS reads, then meets the
+// other wavefronts at a plain barrier: after it, every wave's slab of the next
+// stage is in the LDS and no wave still reads the stage about to be refilled.
+// (An L2 prefetch of the step after next, one dword per line, was measured
+// slower: it only added L2 traffic.)
+__device__ __forceinline__ void wait_loads_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+}
+
 template <class Issue, class Ragged, class Frags, class Compute, class Hint>
 __device__ __forceinline__ void run_main_loop(uint8_t* s0, uint8_t* s1, int nfull, int nk, bool ragged_k,
                                               Issue& issue_direct, Ragged& stage_ragged, Frags& load_frags,
                                               Compute& compute, Hint& interleave) {
-  auto step = [&](uint8_t* __restrict__ nxt, const uint8_t* __restrict__ cur, int kt_next) {
-    issue_direct(nxt, kt_next);
-    // Keep the loads at the head of the step and the MFMAs inside it: left
-    // alone, the scheduler may sink the loads below the MFMAs or the MFMAs
-    // below the barrier, either of which leaves the loads no time to land.
-    __builtin_amdgcn_sched_barrier(0);
-    compute(cur);
+  // The loads of step kt+1 go out in groups between the first MFMA blocks of
+  // step kt (the hook `dma(g)`): issued all at once they back up the wave's
+  // memory-instruction queue and stall its MFMAs.  The MFMAs stay inside their
+  // step (sched_barrier): the scheduler would otherwise sink them below the
+  // barrier, where they no longer hide the loads.
+  auto step = [&](uint8_t* nxt, const uint8_t* cur, int kt_next) {
+    compute(cur, [&](int g) { issue_direct(nxt, kt_next, g); });
     interleave();
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmem();
-    __syncthreads();
+    wait_loads_and_barrier();
     load_frags(nxt);
   };
-  if (nfull > 0) issue_direct(s0, 0); else stage_ragged(0, 0);
-  wait_vmem();
-  __syncthreads();
+  auto no_dma = [](int) {};
+  if (nfull > 0) {
+    for (int g = 0; g < kDmaGroups; ++g) issue_direct(s0, 0, g);
+    wait_loads_and_barrier();
+  } else {
+    stage_ragged(0, 0);
+    wait_vmem();
+    __syncthreads();
+  }
   load_frags(s0);
   int kt = 0;
   for (; kt + 2 < nfull; kt += 2) {
@@ -79,7 +109,7 @@ __device__ __forceinline__ void run_main_loop(uint8_t* s0, uint8_t* s1, int nful
     uint8_t* cur = (kt & 1) ? s1 : s0;
     uint8_t* nxt = (kt & 1) ? s0 : s1;
     if (ragged_k) stage_ragged(kt + 1, (kt & 1) ^ 1);
-    compute(cur);
+    compute(cur, no_dma);
     ++kt;
     if (ragged_k) {
       wait_vmem();
@@ -87,7 +117,8 @@ __device__ __forceinline__ void run_main_loop(uint8_t* s0, uint8_t* s1, int nful
       load_frags(nxt);
     }
   }
-  if (kt < nk) compute((kt & 1) ? s1 : s0);
+  if (kt < nk) compute((kt & 1) ? s1 : s0, no_dma);
+  wait_vmem();  // no load may still be writing the LDS when the epilogue reuses it
 }
 
 // Epilogue: the scaled output tile goes through LDS (free once the K loop is
@@ -179,16 +210,21 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
   const __amdgpu_buffer_rsrc_t rb = operand_rsrc(B + n_base * K, N - n_base, K);
   const int lrow = w * 8 + (lane >> 3);
   const int voff = lrow * K + (((lane & 7) ^ lds_swz(lrow)) & 7) * 16;
-  auto issue_direct = [&](uint8_t* dst, int kt) {
+  // Group g of the loads of step kt into stage `dst`: loads d = g*PER .. of the
+  // wave's LQA + LQB (A first).  A group is pinned where it is issued.
+  auto issue_direct = [&](uint8_t* dst, int kt, int g) {
+    constexpr int PER = (LQA + LQB + kDmaGroups - 1) / kDmaGroups;
     const int k0 = kt * kBK;
+    const uint32_t la = lds_addr(dst) + w * 1024, lb = lds_addr(dst + BM * kBK) + w * 1024;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int q = 0; q < LQA; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(dst + (w + q * NW) * 1024), 16, voff,
-                                               q * NW * 8 * K + k0, 0, 0);
-#pragma unroll
-    for (int q = 0; q < LQB; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(dst + BM * kBK + (w + q * NW) * 1024), 16, voff,
-                                               q * NW * 8 * K + k0, 0, 0);
+    for (int e = 0; e < PER; ++e) {
+      const int d = g * PER + e;
+      if (d >= LQA + LQB) break;
+      if (d < LQA) dma_lds16(ra, la + d * NW * 1024, voff, d * NW * 8 * K + k0);
+      else dma_lds16(rb, lb + (d - LQA) * NW * 1024, voff, (d - LQA) * NW * 8 * K + k0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
   // Zero-filled register path for a ragged last K step.
   auto stage_ragged = [&](int kt, int stage) {
@@ -239,6 +275,7 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
       const uint4 lo = granule(tile, row0, 2 * hh), hi = granule(tile, row0, 2 * hh + 1);
       return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     };
+    static_assert(FN >= kDmaGroups, "one load group per leading B block");
     // A fragments of the step stay in registers; B fragments stream one
     // 16-row block ahead (bf[(j+1)&1] is read while the MFMAs of block j run).
     v8i af[FM], bf[2];
@@ -248,9 +285,10 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
       for (int i = 0; i < FM; ++i) af[i] = frag(st, wm * WTM + i * 16);
     };
     // Contract the stage at `st` (A fragments and the first B fragment already in registers).
-    auto compute = [&](const uint8_t* st) {
+    auto compute = [&](const uint8_t* st, auto&& dma) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
+        if (j < kDmaGroups) dma(j);
         if (j + 1 < FN) bf[(j + 1) & 1] = frag(st + BM * kBK, wn * WTN + (j + 1) * 16);
 #pragma unroll
         for (int i = 0; i < FM; ++i) acc[i][j] = mfma_fp8<FB, FA>(bf[j & 1], af[i], acc[i][j]);
@@ -295,9 +333,10 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
         for (int i = 0; i < FM; ++i) ar[i][c] = granule(st, wm * WTM + i * 32, 4 * hh + c);
       }
     };
-    auto compute = [&](const uint8_t*) {
+    auto compute = [&](const uint8_t*, auto&& dma) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
+        if (s < kDmaGroups) dma(s);
         v8h bh[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
