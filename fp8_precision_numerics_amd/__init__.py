@@ -6,7 +6,7 @@ the HIP sources under csrc/; this package is its Python binding (argument
 marshalling) plus a small holder for one tensor's delayed-scaling buffers.
 """
 
-from ._binding import (ACCUM_EXACT, ACCUM_MFMA_FP8, BF16, E4M3, E5M2, EXPORTED_SYMBOLS, F32, Fp8Error, fp8_amax_update, fp8_gemm,  # noqa: F401
+from ._binding import (ACCUM_EXACT, ACCUM_MFMA_FP8, BF16, E4M3, E5M2, EXPORTED_SYMBOLS, F32, QUANTIZE_WORKSPACE_BYTES, Fp8Error, fp8_amax_update, fp8_gemm,  # noqa: F401
                        fp8_grouped_gemm, fp8_quantize, fp8_quantize_blockwise, library_path, load_library,
                        status_string, version)
 from .state import DelayedScalingState, Recipe  # noqa: F401

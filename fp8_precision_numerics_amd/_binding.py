@@ -15,7 +15,7 @@ import os
 
 import torch
 
-__all__ = ["E4M3", "E5M2", "F32", "BF16", "ACCUM_EXACT", "ACCUM_MFMA_FP8", "Fp8Error", "load_library", "library_path",
+__all__ = ["E4M3", "E5M2", "F32", "BF16", "ACCUM_EXACT", "ACCUM_MFMA_FP8", "QUANTIZE_WORKSPACE_BYTES", "Fp8Error", "load_library", "library_path",
            "status_string", "version", "fp8_quantize", "fp8_amax_update", "fp8_gemm",
            "fp8_quantize_blockwise", "fp8_grouped_gemm", "EXPORTED_SYMBOLS"]
 
@@ -35,6 +35,10 @@ _LIB = None
 
 def library_path() -> str:
     return os.environ.get("FP8MI_LIBRARY", os.path.join(_HERE, "lib", "libfp8mi.so"))
+
+
+# Workspace size that lets a cast grid cover the device (FP8MI_QUANTIZE_WORKSPACE_BYTES).
+QUANTIZE_WORKSPACE_BYTES = 16384
 
 
 class Fp8Error(RuntimeError):
@@ -60,7 +64,8 @@ def load_library():
     lib.fp8mi_status_string.restype = ctypes.c_char_p
     lib.fp8mi_version.argtypes = []
     lib.fp8mi_version.restype = ctypes.c_int
-    lib.fp8_quantize.argtypes = [vp, ctypes.c_int, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp]
+    lib.fp8_quantize.argtypes = [vp, ctypes.c_int, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                 vp]
     lib.fp8_quantize.restype = ctypes.c_int
     lib.fp8_amax_update.argtypes = [vp, i32, vp, vp, ctypes.c_int, vp, vp, vp, vp]
     lib.fp8_amax_update.restype = ctypes.c_int
@@ -150,12 +155,14 @@ def _call(name, status):
 # ---------------------------------------------------------------------------
 # entry points
 # ---------------------------------------------------------------------------
-def fp8_quantize(x, fmt, scale=None, q=None, q_t=None, amax=None, sat=None, stream=None) -> None:
+def fp8_quantize(x, fmt, scale=None, q=None, q_t=None, amax=None, sat=None, workspace=None, stream=None) -> None:
     """Fused amax + scaled saturating cast of x ([rows x cols], fp32 or bf16).
 
     q: uint8 [rows x cols] or None; q_t: uint8 [cols x rows] or None;
     scale: fp32[1] device scale; amax: fp32[1] (overwritten); sat: int64[1]
-    (overwritten with the saturated-element count).
+    (overwritten with the saturated-element count); workspace: optional uint8
+    device scratch (QUANTIZE_WORKSPACE_BYTES lets the grid cover the device) for
+    the per-workgroup partials of amax and the count.
     """
     lib = load_library()
     _check(x, "x", (torch.float32, torch.bfloat16))
@@ -166,9 +173,12 @@ def fp8_quantize(x, fmt, scale=None, q=None, q_t=None, amax=None, sat=None, stre
     _check(q_t, "q_t", torch.uint8, rows * cols, dev)
     _check(amax, "amax", torch.float32, 1, dev)
     _check(sat, "sat", torch.int64, 1, dev)
+    _check(workspace, "workspace", torch.uint8, None, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel()
     with torch.cuda.device(dev):
         _call("fp8_quantize", lib.fp8_quantize(_p(x), _xtype(x), rows, cols, _fmt(fmt), _p(scale), _p(q),
-                                               _p(q_t), _p(amax), _p(sat), _stream(stream)))
+                                               _p(q_t), _p(amax), _p(sat), _p(workspace), ws_bytes,
+                                               _stream(stream)))
 
 
 def fp8_amax_update(history, head, amax, fmt, scale, scale_inv, status=None, stream=None) -> None:

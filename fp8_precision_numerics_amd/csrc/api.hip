@@ -65,10 +65,11 @@ const char* fp8mi_status_string(int status) {
   }
 }
 
-int fp8mi_version(void) { return 200; }
+int fp8mi_version(void) { return 300; }
 
 int fp8_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, const float* scale,
-                 uint8_t* q, uint8_t* q_t, float* amax, unsigned long long* sat, void* stream) {
+                 uint8_t* q, uint8_t* q_t, float* amax, unsigned long long* sat, void* workspace,
+                 size_t workspace_bytes, void* stream) {
   if (!dtype_ok(xtype)) return FP8MI_ERR_DTYPE;
   if (!fmt_ok(fmt)) return FP8MI_ERR_FORMAT;
   if (!dims_ok(rows, cols)) return FP8MI_ERR_SHAPE;
@@ -78,13 +79,14 @@ int fp8_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, 
   if (n > 0 && !x) return FP8MI_ERR_NULL;
   if ((x && !aligned16(x)) || (q && !aligned16(q)) || (q_t && !aligned16(q_t))) return FP8MI_ERR_ALIGN;
   if (q_t && ((rows & 15) || (cols & 15))) return FP8MI_ERR_ALIGN;
+  if (workspace && (!aligned16(workspace) || workspace_bytes < 16)) return FP8MI_ERR_ALIGN;
   if (q_t && (rows + 127) / 128 > 65535) return FP8MI_ERR_SHAPE;
   if ((cols + 127) / 128 > kMaxDim) return FP8MI_ERR_SHAPE;
   if (!amax && !sat && n == 0) return FP8MI_OK;
   const int dev = check_device();
   if (dev != FP8MI_OK) return dev;
-  return launched(fp8mi::launch_quantize(x, xtype, rows, cols, fmt, scale, q, q_t, amax, sat,
-                                         (hipStream_t)stream));
+  return launched(fp8mi::launch_quantize(x, xtype, rows, cols, fmt, scale, q, q_t, amax, sat, workspace,
+                                         workspace_bytes, (hipStream_t)stream));
 }
 
 int fp8_amax_update(float* history, int32_t history_len, int32_t* head, const float* amax, int fmt,

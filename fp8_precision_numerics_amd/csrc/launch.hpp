@@ -10,7 +10,8 @@ namespace fp8mi {
 
 hipError_t launch_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt,
                            const float* scale, uint8_t* q, uint8_t* q_t, float* amax,
-                           unsigned long long* sat, hipStream_t stream);
+                           unsigned long long* sat, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 hipError_t launch_quantize_blockwise(const void* x, int xtype, int64_t rows, int64_t cols,
                                      int block_rows, int fmt, uint8_t* q, float* scale_inv,

@@ -34,9 +34,14 @@ __global__ void zero_outputs_kernel(uint32_t* amax_bits, unsigned long long* sat
   }
 }
 
-// Fold (per-lane amax bits, per-wave saturation count) into the global outputs.
+// Fold (per-lane amax bits, per-wave saturation count) into the global outputs:
+// either one partial per workgroup (`partials` non-null: slot blockIdx.x gets
+// {amax bits, 0, count lo, count hi}, reduced afterwards by
+// reduce_partials_kernel) or device-scope atomics on the outputs.  The atomics
+// on one address are serialised across the chip (about 4 ns each on MI355X,
+// ~4 us for a 512-workgroup grid); the partials cost one tiny extra kernel.
 __device__ __forceinline__ void block_finish(uint32_t amx, uint32_t wave_cnt, uint32_t* amax_bits,
-                                             unsigned long long* sat) {
+                                             unsigned long long* sat, uint4* partials) {
   __shared__ uint32_t s_max[kWaves];
   __shared__ uint32_t s_cnt[kWaves];
   amx = wave_max_u32(amx);
@@ -54,8 +59,45 @@ __device__ __forceinline__ void block_finish(uint32_t amx, uint32_t wave_cnt, ui
       m = m > s_max[w] ? m : s_max[w];
       c += s_cnt[w];
     }
-    if (amax_bits) atomicMax(amax_bits, m);
-    if (sat && c) atomicAdd(sat, c);
+    if (partials) {
+      partials[blockIdx.x] = make_uint4(m, 0u, (uint32_t)c, (uint32_t)(c >> 32));
+    } else {
+      if (amax_bits) atomicMax(amax_bits, m);
+      if (sat && c) atomicAdd(sat, c);
+    }
+  }
+}
+
+// Reduce `count` workgroup partials into the outputs (one workgroup).
+__global__ __launch_bounds__(kThreads) void reduce_partials_kernel(const uint4* __restrict__ partials, int count,
+                                                                  uint32_t* __restrict__ amax_bits,
+                                                                  unsigned long long* __restrict__ sat) {
+  __shared__ uint32_t s_max[kWaves];
+  __shared__ unsigned long long s_cnt[kWaves];
+  uint32_t m = 0u;
+  unsigned long long c = 0ull;
+  for (int i = threadIdx.x; i < count; i += kThreads) {
+    const uint4 p = partials[i];
+    m = m > p.x ? m : p.x;
+    c += (unsigned long long)p.z | ((unsigned long long)p.w << 32);
+  }
+  m = wave_max_u32(m);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    s_max[wave] = m;
+    s_cnt[wave] = c;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {  // holds wave 0's totals
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      m = m > s_max[w] ? m : s_max[w];
+      c += s_cnt[w];
+    }
+    if (amax_bits) *amax_bits = m;
+    if (sat) *sat = c;
   }
 }
 
@@ -123,7 +165,7 @@ constexpr int kVecPerLane = 4;
 template <int XT, int FMT, bool WQ, bool SAT>
 __global__ __launch_bounds__(kThreads) void quantize_flat_kernel(
     const void* __restrict__ x, int64_t n, const float* __restrict__ scale, uint8_t* __restrict__ q,
-    uint32_t* __restrict__ amax_bits, unsigned long long* __restrict__ sat) {
+    uint32_t* __restrict__ amax_bits, unsigned long long* __restrict__ sat, uint4* __restrict__ partials) {
   constexpr int EPV = Vec<XT>::EPV, U = kVecPerLane;
   const float s = (WQ || SAT) ? *scale : 1.0f;
   const bool regular = scale_is_regular(s);
@@ -183,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void quantize_flat_kernel(
     }
     if constexpr (WQ) q[i] = encode1<FMT>(p);
   }
-  block_finish(amx, wcnt, amax_bits, sat);
+  block_finish(amx, wcnt, amax_bits, sat, partials);
 }
 
 // ---------------------------------------------------------------------------
@@ -214,7 +256,7 @@ template <int XT, int FMT, bool WQ, bool SAT>
 __global__ __launch_bounds__(kThreads) void quantize_transpose_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, const float* __restrict__ scale,
     uint8_t* __restrict__ q, uint8_t* __restrict__ q_t, uint32_t* __restrict__ amax_bits,
-    unsigned long long* __restrict__ sat) {
+    unsigned long long* __restrict__ sat, uint4* __restrict__ partials) {
   constexpr int EPV = Vec<XT>::EPV;
   constexpr int VPR = kTile / EPV;          // vectors per tile row
   constexpr int RPP = kThreads / VPR;       // tile rows per pass
@@ -287,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void quantize_transpose_kernel(
   }
   __syncthreads();  // the LDS tile is rewritten by the next iteration
   }
-  block_finish(amx, wcnt, amax_bits, sat);
+  block_finish(amx, wcnt, amax_bits, sat, partials);
 }
 
 // ---------------------------------------------------------------------------
@@ -405,59 +447,65 @@ int persistent_groups() {
   return cached[dev];
 }
 
-template <int XT, int FMT, bool WQ, bool SAT>
-void launch_flat_t(const void* x, int64_t n, const float* scale, uint8_t* q, uint32_t* amax_bits,
-                   unsigned long long* sat, hipStream_t st) {
-  constexpr int EPV = Vec<XT>::EPV;
-  const int64_t per_block = (int64_t)kThreads * kVecPerLane;
-  int64_t g = (n / EPV + per_block - 1) / per_block;
+// Workgroups of a cast grid with `partials` slots available (0: no limit).
+int cast_groups(int64_t units, int64_t per_group, int64_t slots) {
+  int64_t g = (units + per_group - 1) / per_group;
   if (g > persistent_groups()) g = persistent_groups();
-  if (g < 1) g = 1;
+  if (slots > 0 && g > slots) g = slots;
+  return g < 1 ? 1 : (int)g;
+}
+
+template <int XT, int FMT, bool WQ, bool SAT>
+int launch_flat_t(const void* x, int64_t n, const float* scale, uint8_t* q, uint32_t* amax_bits,
+                  unsigned long long* sat, uint4* partials, int64_t slots, hipStream_t st) {
+  constexpr int EPV = Vec<XT>::EPV;
+  const int g = cast_groups(n / EPV, (int64_t)kThreads * kVecPerLane, partials ? slots : 0);
   hipLaunchKernelGGL((quantize_flat_kernel<XT, FMT, WQ, SAT>), dim3((unsigned)g), dim3(kThreads), 0, st, x, n,
-                     scale, q, amax_bits, sat);
+                     scale, q, amax_bits, sat, partials);
+  return g;
 }
 
 template <int XT, int FMT>
-void launch_flat_f(const void* x, int64_t n, const float* scale, uint8_t* q, uint32_t* amax_bits,
-                   unsigned long long* sat, hipStream_t st) {
-  if (q && sat) launch_flat_t<XT, FMT, true, true>(x, n, scale, q, amax_bits, sat, st);
-  else if (q) launch_flat_t<XT, FMT, true, false>(x, n, scale, q, amax_bits, sat, st);
-  else if (sat) launch_flat_t<XT, FMT, false, true>(x, n, scale, q, amax_bits, sat, st);
-  else launch_flat_t<XT, FMT, false, false>(x, n, scale, q, amax_bits, sat, st);
+int launch_flat_f(const void* x, int64_t n, const float* scale, uint8_t* q, uint32_t* amax_bits,
+                  unsigned long long* sat, uint4* partials, int64_t slots, hipStream_t st) {
+  if (q && sat) return launch_flat_t<XT, FMT, true, true>(x, n, scale, q, amax_bits, sat, partials, slots, st);
+  if (q) return launch_flat_t<XT, FMT, true, false>(x, n, scale, q, amax_bits, sat, partials, slots, st);
+  if (sat) return launch_flat_t<XT, FMT, false, true>(x, n, scale, q, amax_bits, sat, partials, slots, st);
+  return launch_flat_t<XT, FMT, false, false>(x, n, scale, q, amax_bits, sat, partials, slots, st);
 }
 
 template <int XT, int FMT>
-void launch_transpose_f(const void* x, int64_t rows, int64_t cols, const float* scale, uint8_t* q,
-                        uint8_t* q_t, uint32_t* amax_bits, unsigned long long* sat,
-                        hipStream_t st) {
-  int64_t tiles = ((cols + kTile - 1) / kTile) * ((rows + kTile - 1) / kTile);
-  const dim3 grid((unsigned)(tiles < persistent_groups() ? tiles : persistent_groups()));
+int launch_transpose_f(const void* x, int64_t rows, int64_t cols, const float* scale, uint8_t* q, uint8_t* q_t,
+                       uint32_t* amax_bits, unsigned long long* sat, uint4* partials, int64_t slots,
+                       hipStream_t st) {
+  const int64_t tiles = ((cols + kTile - 1) / kTile) * ((rows + kTile - 1) / kTile);
+  const dim3 grid((unsigned)cast_groups(tiles, 1, partials ? slots : 0));
   if (q && sat)
     hipLaunchKernelGGL((quantize_transpose_kernel<XT, FMT, true, true>), grid, dim3(kThreads), 0, st,
-                       x, rows, cols, scale, q, q_t, amax_bits, sat);
+                       x, rows, cols, scale, q, q_t, amax_bits, sat, partials);
   else if (q)
     hipLaunchKernelGGL((quantize_transpose_kernel<XT, FMT, true, false>), grid, dim3(kThreads), 0,
-                       st, x, rows, cols, scale, q, q_t, amax_bits, sat);
+                       st, x, rows, cols, scale, q, q_t, amax_bits, sat, partials);
   else if (sat)
     hipLaunchKernelGGL((quantize_transpose_kernel<XT, FMT, false, true>), grid, dim3(kThreads), 0,
-                       st, x, rows, cols, scale, q, q_t, amax_bits, sat);
+                       st, x, rows, cols, scale, q, q_t, amax_bits, sat, partials);
   else
     hipLaunchKernelGGL((quantize_transpose_kernel<XT, FMT, false, false>), grid, dim3(kThreads), 0,
-                       st, x, rows, cols, scale, q, q_t, amax_bits, sat);
+                       st, x, rows, cols, scale, q, q_t, amax_bits, sat, partials);
+  return (int)grid.x;
 }
 
 template <int XT>
-void launch_quantize_x(const void* x, int64_t rows, int64_t cols, int fmt, const float* scale,
-                       uint8_t* q, uint8_t* q_t, uint32_t* amax_bits, unsigned long long* sat,
-                       hipStream_t st) {
+int launch_quantize_x(const void* x, int64_t rows, int64_t cols, int fmt, const float* scale, uint8_t* q,
+                      uint8_t* q_t, uint32_t* amax_bits, unsigned long long* sat, uint4* partials, int64_t slots,
+                      hipStream_t st) {
   const int64_t n = rows * cols;
   if (q_t) {
-    if (fmt == kE4M3) launch_transpose_f<XT, kE4M3>(x, rows, cols, scale, q, q_t, amax_bits, sat, st);
-    else launch_transpose_f<XT, kE5M2>(x, rows, cols, scale, q, q_t, amax_bits, sat, st);
-  } else {
-    if (fmt == kE4M3) launch_flat_f<XT, kE4M3>(x, n, scale, q, amax_bits, sat, st);
-    else launch_flat_f<XT, kE5M2>(x, n, scale, q, amax_bits, sat, st);
+    if (fmt == kE4M3) return launch_transpose_f<XT, kE4M3>(x, rows, cols, scale, q, q_t, amax_bits, sat, partials, slots, st);
+    return launch_transpose_f<XT, kE5M2>(x, rows, cols, scale, q, q_t, amax_bits, sat, partials, slots, st);
   }
+  if (fmt == kE4M3) return launch_flat_f<XT, kE4M3>(x, n, scale, q, amax_bits, sat, partials, slots, st);
+  return launch_flat_f<XT, kE5M2>(x, n, scale, q, amax_bits, sat, partials, slots, st);
 }
 
 template <int XT, int FMT>
@@ -480,16 +528,24 @@ void launch_blockwise_t(const void* x, int64_t rows, int64_t cols, int block_row
 
 hipError_t launch_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt,
                            const float* scale, uint8_t* q, uint8_t* q_t, float* amax,
-                           unsigned long long* sat, hipStream_t stream) {
+                           unsigned long long* sat, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
   uint32_t* amax_bits = reinterpret_cast<uint32_t*>(amax);
-  if (amax_bits || sat)
-    hipLaunchKernelGGL(zero_outputs_kernel, dim3(1), dim3(64), 0, stream, amax_bits, sat);
+  const bool reduce = amax_bits || sat;
+  // With a workspace: per-workgroup partials, then one small reduction kernel.
+  // Without: clear the outputs, then device-scope atomics per workgroup.
+  uint4* partials = (reduce && workspace) ? reinterpret_cast<uint4*>(workspace) : nullptr;
+  const int64_t slots = (int64_t)(workspace_bytes / sizeof(uint4));
+  if (reduce && !partials) hipLaunchKernelGGL(zero_outputs_kernel, dim3(1), dim3(64), 0, stream, amax_bits, sat);
+  int groups = 0;
   if (rows * cols > 0) {
     if (xtype == kBF16)
-      launch_quantize_x<kBF16>(x, rows, cols, fmt, scale, q, q_t, amax_bits, sat, stream);
+      groups = launch_quantize_x<kBF16>(x, rows, cols, fmt, scale, q, q_t, amax_bits, sat, partials, slots, stream);
     else
-      launch_quantize_x<kF32>(x, rows, cols, fmt, scale, q, q_t, amax_bits, sat, stream);
+      groups = launch_quantize_x<kF32>(x, rows, cols, fmt, scale, q, q_t, amax_bits, sat, partials, slots, stream);
   }
+  if (partials)
+    hipLaunchKernelGGL(reduce_partials_kernel, dim3(1), dim3(kThreads), 0, stream, partials, groups, amax_bits, sat);
   return hipGetLastError();
 }
 

@@ -49,10 +49,12 @@ class DelayedScalingState:
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         self.amax = torch.zeros(1, dtype=torch.float32, device=dev)
         self.sat = torch.zeros(1, dtype=torch.int64, device=dev)
+        # scratch for the per-workgroup partials of amax and the count
+        self.workspace = torch.empty(_b.QUANTIZE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
 
     def quantize(self, x, q=None, q_t=None, count_saturation=False, stream=None):
         _b.fp8_quantize(x, self.fmt, self.scale, q=q, q_t=q_t, amax=self.amax,
-                        sat=self.sat if count_saturation else None, stream=stream)
+                        sat=self.sat if count_saturation else None, workspace=self.workspace, stream=stream)
 
     def update(self, stream=None):
         _b.fp8_amax_update(self.history, self.head, self.amax, self.fmt, self.scale, self.scale_inv,

@@ -36,6 +36,7 @@
 #ifndef FP8MI_H
 #define FP8MI_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #if defined(__GNUC__) || defined(__clang__)
@@ -106,12 +107,21 @@ FP8MI_API int fp8mi_version(void);
  *          multiples of 16.
  * amax     device, 1 fp32, overwritten (not accumulated), or NULL.
  * sat      device, 1 uint64, overwritten, or NULL.
+ * workspace  device scratch owned by the caller, 16-B aligned, or NULL.  With
+ *          one, each workgroup writes its partial amax / count into it and a
+ *          small second kernel reduces them (no contended atomics); up to
+ *          workspace_bytes / 16 workgroups are used, so FP8MI_QUANTIZE_WORKSPACE_BYTES
+ *          lets the grid cover the device.  Contents on entry do not matter;
+ *          two calls in flight at once must not share one workspace.  Without
+ *          one, the outputs are cleared and then updated with atomics.
  * At least one of q, q_t, amax must be non-NULL.  rows*cols may be 0 (then
  * amax = 0 and sat = 0).
  */
+#define FP8MI_QUANTIZE_WORKSPACE_BYTES 16384
+
 FP8MI_API int fp8_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt,
                  const float* scale, uint8_t* q, uint8_t* q_t, float* amax,
-                 unsigned long long* sat, void* stream);
+                 unsigned long long* sat, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * fp8_amax_update — delayed-scaling history step ([TE] §4.2.4 "delayed

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert fm.version() == 200
+    assert fm.version() == 300
     for code in (OK, ENULL, ESHAPE, EALIGN, EFMT, EDTYPE, ELAUNCH, EDEV, EACCUM):
         assert fm.status_string(code) and fm.status_string(code) != "unknown status"
     assert fm.status_string(12345) == "unknown status"
@@ -50,18 +50,20 @@ def test_version_and_status_strings(lib):
 
 def test_quantize_argument_errors(lib):
     q = lib.fp8_quantize
-    assert q(A16, 7, 4, 16, 0, A16, A16, None, None, None, None) == EDTYPE
-    assert q(A16, 0, 4, 16, 9, A16, A16, None, None, None, None) == EFMT
-    assert q(A16, 0, -1, 16, 0, A16, A16, None, None, None, None) == ESHAPE
-    assert q(A16, 0, 1 << 40, 1 << 40, 0, A16, A16, None, None, None, None) == ESHAPE
-    assert q(A16, 0, 4, 16, 0, A16, None, None, None, None, None) == ENULL      # no output at all
-    assert q(A16, 0, 4, 16, 0, None, A16, None, None, None, None) == ENULL      # cast without a scale
-    assert q(None, 0, 4, 16, 0, A16, A16, None, None, None, None) == ENULL
-    assert q(A8, 0, 4, 16, 0, A16, A16, None, None, None, None) == EALIGN
-    assert q(A16, 0, 4, 16, 0, A16, A8, None, None, None, None) == EALIGN
-    assert q(A16, 0, 4, 24, 0, A16, None, A16, None, None, None) == EALIGN      # transpose needs 16 | cols
-    assert q(A16, 0, 20, 16, 0, A16, None, A16, None, None, None) == EALIGN     # ... and 16 | rows
-    assert q(None, 0, 0, 16, 0, A16, A16, None, None, None, None) == OK         # empty, no reductions
+    assert q(A16, 7, 4, 16, 0, A16, A16, None, None, None, None, 0, None) == EDTYPE
+    assert q(A16, 0, 4, 16, 9, A16, A16, None, None, None, None, 0, None) == EFMT
+    assert q(A16, 0, -1, 16, 0, A16, A16, None, None, None, None, 0, None) == ESHAPE
+    assert q(A16, 0, 1 << 40, 1 << 40, 0, A16, A16, None, None, None, None, 0, None) == ESHAPE
+    assert q(A16, 0, 4, 16, 0, A16, None, None, None, None, None, 0, None) == ENULL      # no output at all
+    assert q(A16, 0, 4, 16, 0, None, A16, None, None, None, None, 0, None) == ENULL      # cast without a scale
+    assert q(None, 0, 4, 16, 0, A16, A16, None, None, None, None, 0, None) == ENULL
+    assert q(A8, 0, 4, 16, 0, A16, A16, None, None, None, None, 0, None) == EALIGN
+    assert q(A16, 0, 4, 16, 0, A16, A8, None, None, None, None, 0, None) == EALIGN
+    assert q(A16, 0, 4, 24, 0, A16, None, A16, None, None, None, 0, None) == EALIGN      # transpose needs 16 | cols
+    assert q(A16, 0, 20, 16, 0, A16, None, A16, None, None, None, 0, None) == EALIGN     # ... and 16 | rows
+    assert q(None, 0, 0, 16, 0, A16, A16, None, None, None, None, 0, None) == OK         # empty, no reductions
+    assert q(A16, 0, 4, 16, 0, A16, A16, None, A16, None, A8, 64, None) == EALIGN       # workspace alignment
+    assert q(A16, 0, 4, 16, 0, A16, A16, None, A16, None, A16, 8, None) == EALIGN       # workspace < 16 B
 
 
 def test_amax_update_argument_errors(lib):

@@ -16,7 +16,16 @@ FMTS = ["e4m3", "e5m2"]
 SCALES = [1.0, 14933.333984375, 0.448, 3.0e-3, 1.7e35, 2.0 ** -20]
 
 
-def gpu_quantize(x: torch.Tensor, fmt, scale, transpose=False, rowmajor=True, count=True):
+def workspace_for(ws, dev):
+    """None (atomics path), a full workspace or a 16-byte one (a single
+    workgroup), filled with junk: its contents on entry must not matter."""
+    if not ws:
+        return None
+    size = fm.QUANTIZE_WORKSPACE_BYTES if ws == "full" else 16
+    return torch.full((size,), 0xAB, dtype=torch.uint8, device=dev)
+
+
+def gpu_quantize(x: torch.Tensor, fmt, scale, transpose=False, rowmajor=True, count=True, ws=None):
     dev = x.device
     rows, cols = (x.shape[0], x.shape[1]) if x.dim() == 2 else (1, x.numel())
     s = torch.tensor([scale], dtype=torch.float32, device=dev)
@@ -24,7 +33,7 @@ def gpu_quantize(x: torch.Tensor, fmt, scale, transpose=False, rowmajor=True, co
     qt = torch.empty(rows * cols, dtype=torch.uint8, device=dev) if transpose else None
     amax = torch.full((1,), 12345.0, dtype=torch.float32, device=dev)   # must be overwritten
     sat = torch.full((1,), 777, dtype=torch.int64, device=dev) if count else None
-    fm.fp8_quantize(x, fmt, s, q=q, q_t=qt, amax=amax, sat=sat)
+    fm.fp8_quantize(x, fmt, s, q=q, q_t=qt, amax=amax, sat=sat, workspace=workspace_for(ws, dev))
     torch.cuda.synchronize()
     return q, qt, amax, sat
 
@@ -39,9 +48,10 @@ def test_adversarial_fp32_values_bit_exact(fmt):
     n = x.size - x.size % 16 + 7            # leave a ragged tail of 7 elements
     x = np.ascontiguousarray(x[:n])
     xd = to_device((x, "f32"))
-    for s in SCALES:
-        announce(f"adversarial fp32 n={n} fmt={fmt} scale={s}")
-        q, _, amax, sat = gpu_quantize(xd, fmt, s)
+    for i, s in enumerate(SCALES):
+        wsp = ("full", None, "tiny")[i % 3]
+        announce(f"adversarial fp32 n={n} fmt={fmt} scale={s} workspace={wsp}")
+        q, _, amax, sat = gpu_quantize(xd, fmt, s, ws=wsp)
         wq, wa, ws = oracle_quantize(x, fmt, s)
         bad = np.flatnonzero(u8(q) != wq)
         assert bad.size == 0, [(hex(int(x.view(np.uint32)[i])), hex(int(u8(q)[i])), hex(int(wq[i])))
@@ -55,9 +65,10 @@ def test_every_bf16_value_bit_exact(fmt):
     bits = np.arange(1 << 16, dtype=np.uint16)
     xd = to_device((bits.reshape(256, 256), "bf16"))
     x32 = scaling.widen(bits, "bf16")
-    for s in SCALES:
-        announce(f"all bf16 values fmt={fmt} scale={s}")
-        q, qt, amax, sat = gpu_quantize(xd, fmt, s, transpose=True)
+    for i, s in enumerate(SCALES):
+        wsp = ("full", None, "tiny")[i % 3]
+        announce(f"all bf16 values fmt={fmt} scale={s} workspace={wsp}")
+        q, qt, amax, sat = gpu_quantize(xd, fmt, s, transpose=True, ws=wsp)
         wq, wa, ws = oracle_quantize(x32, fmt, s)
         assert np.array_equal(u8(q), wq)
         assert np.array_equal(u8(qt).reshape(256, 256), wq.reshape(256, 256).T)
@@ -65,10 +76,11 @@ def test_every_bf16_value_bit_exact(fmt):
         assert int(sat.item()) == ws
 
 
+@pytest.mark.parametrize("wsp", [None, "full"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("shape", [(16, 16), (128, 128), (144, 272), (400, 1040), (1, 33), (3, 5)])
-def test_shapes_rowmajor_and_transpose(shape, fmt, dtype):
+def test_shapes_rowmajor_and_transpose(shape, fmt, dtype, wsp):
     rng = np.random.default_rng(shape[0] * 7919 + shape[1] * 31 + FMTS.index(fmt) * 2 + (dtype == "bf16"))
     x32 = (rng.standard_normal(shape) * 10.0 ** rng.uniform(-2, 3, size=shape)).astype(np.float32)
     h = HostTensor(x32, "f32") if dtype == "f32" else HostTensor(bf16_bits_from_f32(x32), "bf16")
@@ -76,8 +88,8 @@ def test_shapes_rowmajor_and_transpose(shape, fmt, dtype):
     xd = to_device(h)
     s = float(scaling.scale_from_amax(scaling.amax(xw) * np.float32(0.7), codec.FORMATS[fmt].max_value)[1])
     tr = shape[0] % 16 == 0 and shape[1] % 16 == 0
-    announce(f"shape {shape} dtype {dtype} fmt {fmt} transpose={tr}")
-    q, qt, amax, sat = gpu_quantize(xd, fmt, s, transpose=tr)
+    announce(f"shape {shape} dtype {dtype} fmt {fmt} transpose={tr} workspace={wsp}")
+    q, qt, amax, sat = gpu_quantize(xd, fmt, s, transpose=tr, ws=wsp)
     wq, wa, ws = oracle_quantize(xw, fmt, s)
     assert np.array_equal(u8(q).reshape(shape), wq)
     if tr:
@@ -100,13 +112,14 @@ def test_transpose_only_and_amax_only():
     assert amax_only.item() == wa
 
 
-def test_empty_tensor_zeroes_reductions():
+@pytest.mark.parametrize("wsp", [None, "full"])
+def test_empty_tensor_zeroes_reductions(wsp):
     dev = device()
     x = torch.empty((0, 16), dtype=torch.float32, device=dev)
     amax = torch.full((1,), 5.0, device=dev)
     sat = torch.full((1,), 9, dtype=torch.int64, device=dev)
     fm.fp8_quantize(x, "e4m3", torch.ones(1, device=dev), q=torch.empty(0, dtype=torch.uint8, device=dev),
-                    amax=amax, sat=sat)
+                    amax=amax, sat=sat, workspace=workspace_for(wsp, dev))
     torch.cuda.synchronize()
     assert amax.item() == 0.0 and sat.item() == 0
 
