@@ -2,9 +2,9 @@
 // the host-side dispatch).
 //
 // Main loop of one workgroup, per 128-deep K step t (stage = t % 2):
-//   * the direct-to-LDS loads of step t+1 into the other stage are issued at
-//     the start of step t and only waited for at the end of the step, so
-//     their latency overlaps the whole step;
+//   * the direct-to-LDS loads of step t+1 into the other stage are issued in
+//     groups between the first MFMA blocks of step t and only waited for at
+//     the end of the step, so their latency overlaps the step;
 //   * FP8 path: the wave's A fragments for step t are in registers; its B
 //     fragments are read one 16-row block ahead (bf[(j+1)&1] while the MFMAs
 //     of block j run).  fp16 path: all raw FP8 fragments of the step are in

@@ -5,9 +5,9 @@
 // * kAccumExact — every product exact, sums in fp32.  The FP8 codes are
 //   widened in registers to fp16 (exact for both E4M3 and E5M2, subnormals
 //   included: V_CVT_SCALEF32_PK_F16_FP8/BF8 with scale 1) and contracted with
-//   V_MFMA_F32_16X16X32_F16.  This is "GEMM in FP8, FP32 accumulation" in the
-//   sense of "4.2 Hopper I — Transformer Engine·FP8" §4.2.4: the result
-//   meets 1e-5·Σ|ab| for every input.
+//   V_MFMA_F32_32X32X16_F16 (no loss was found in its fp32 sums).  This is
+//   "GEMM in FP8, FP32 accumulation" in the sense of "4.2 Hopper I — Transformer
+//   Engine·FP8" §4.2.4: the result meets 1e-5·Σ|ab| for every input.
 //
 // * kAccumMfma8 — the native FP8 matrix-core instruction
 //   V_MFMA_F32_16X16X128_F8F6F4.  Measured on MI355X: it forms dot products of
@@ -17,15 +17,14 @@
 //   truncation (at most 8·2^-13 of the group's largest product) is its
 //   accuracy price.
 //
-// Operand lanes: lane l of the wave supplies row (l % 16) of each operand and
-// the 32-byte K slice (l / 16) of the 128-deep K step.  The kernels feed the B
-// tile (rows = n) as the instruction's first operand and the A tile (rows = m)
-// as its second, so the 16x16 result block is Cᵀ: lane l holds row
-// m = l % 16 and FOUR CONSECUTIVE columns n = 4*(l/16) .. +3, which the
-// epilogue stores as one 8-B (bf16) / 16-B (fp32) vector.  The fp16 path uses
-// bytes [8s, 8s+8) of the same 32-byte slice for its K sub-step s = 0..3:
-// any assignment of K values to (lane, register) slots works as long as both
-// operands use the same one.
+// Operand lanes.  16x16x128 (FP8 path): lane l supplies row l % 16 of each
+// operand and the 32-byte K slice l / 16 of the 128-deep K step.  32x32x16
+// (fp16 path): lane l supplies row l % 32 and the 64-byte half l / 32 of the
+// step, of which sub-step s (16 deep) takes bytes [8s, 8s+8).  Any assignment
+// of K values to (lane, register) slots works as long as both operands use the
+// same one.  The kernels feed the B tile (rows = n) as the instruction's first
+// operand and the A tile (rows = m) as its second, so each lane's accumulators
+// hold one output row m and runs of FOUR CONSECUTIVE columns n.
 //
 // Operand tiles live in LDS as rows of 128 bytes (one K step); the 16-byte
 // granule g of row r sits at position g ^ swz(r) with
@@ -47,8 +46,6 @@ enum : int { kAccumExact = 0, kAccumMfma8 = 1 };
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void global_void_t;
 
 __device__ __forceinline__ int lds_swz(int row) { return (row & 6) | ((row >> 3) & 1); }
 __device__ __forceinline__ int lds_granule(int row, int g) { return row * kBK + (((g ^ lds_swz(row)) & 7) << 4); }
@@ -77,44 +74,9 @@ __device__ __forceinline__ v8h widen8(uint32_t w0, uint32_t w1) {
   return (v8h){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// Read the 32-byte K slice of one fragment row for this lane from an LDS tile.
-__device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int lane) {
-  const int kg = (lane >> 4) * 2;
-  const uint4 lo = *reinterpret_cast<const uint4*>(tile + lds_granule(row, kg));
-  const uint4 hi = *reinterpret_cast<const uint4*>(tile + lds_granule(row, kg + 1));
-  v8i r;
-  r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
-  r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
-  return r;
-}
-
-// Move ROWS x 128 bytes (rows row0.. of a row-major byte matrix with row
-// stride ld, column offset k0) into an LDS tile with direct-to-LDS loads: one
-// wave instruction fills 8 rows (1 KiB; lane i writes bytes [16i, 16i+16) of
-// it), so lane i fetches the granule that belongs at position i & 7 of row
-// i >> 3 of that group.  Rows past `rows_valid` are clamped to the last valid
-// row: they only feed output rows or columns that are never stored.  The
-// caller waits for vmcnt before use.
-template <int ROWS, int NW>
-__device__ __forceinline__ void tile_load_direct(const uint8_t* __restrict__ base, int64_t ld,
-                                                 int64_t row0, int64_t rows_valid, int k0,
-                                                 uint8_t* lds_tile, int wave, int lane) {
-  constexpr int GROUPS = ROWS / 8;
-  static_assert(GROUPS % NW == 0, "tile rows must split evenly over the wavefronts");
-  const int r_in = lane >> 3;
-#pragma unroll
-  for (int q = 0; q < GROUPS / NW; ++q) {
-    const int grp = wave + q * NW;
-    const int g = ((lane & 7) ^ lds_swz(grp * 8 + r_in)) & 7;
-    int64_t r = row0 + grp * 8 + r_in;
-    r = r < rows_valid ? r : rows_valid - 1;
-    const uint8_t* src = base + r * ld + k0 + g * 16;
-    __builtin_amdgcn_global_load_lds((global_void_t*)src, (lds_void_t*)(lds_tile + grp * 1024), 16, 0, 0);
-  }
-}
-
-// Same tile, staged through registers with zero fill for k >= K (the ragged
-// last K step) and for rows past the edge.
+// A ROWS x 128-byte slab (rows row0.. of a row-major byte matrix with row
+// stride ld, column offset k0) staged into an LDS tile through registers, with
+// zero fill for k >= K (the ragged last K step) and for rows past the edge.
 template <int ROWS, int NT>
 __device__ __forceinline__ void tile_load_zero_fill(const uint8_t* __restrict__ base, int64_t ld,
                                                     int64_t row0, int64_t rows_valid, int k0, int K,
@@ -152,70 +114,6 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
   const int local = pid - gid * in_group;
   *tm = first_m + local % gsize;
   *tn = local / gsize;
-}
-
-template <int OUT>
-__device__ __forceinline__ void store4(void* C, int64_t N, int64_t m, int64_t n, int64_t M,
-                                       const v4f& v, bool vec_ok) {
-  if (m >= M) return;
-  if (OUT == kF32) {
-    float* c = reinterpret_cast<float*>(C) + m * N + n;
-    if (vec_ok && n + 3 < N) {
-      *reinterpret_cast<v4f*>(c) = v;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n + j < N) c[j] = v[j];
-    }
-  } else {
-    __bf16* c = reinterpret_cast<__bf16*>(C) + m * N + n;
-    const v2bf lo = __builtin_convertvector((v2f){v[0], v[1]}, v2bf);
-    const v2bf hi = __builtin_convertvector((v2f){v[2], v[3]}, v2bf);
-    if (vec_ok && n + 3 < N) {
-      uint2 w;
-      w.x = __builtin_bit_cast(uint32_t, lo);
-      w.y = __builtin_bit_cast(uint32_t, hi);
-      *reinterpret_cast<uint2*>(c) = w;
-    } else {
-      if (n + 0 < N) c[0] = lo[0];
-      if (n + 1 < N) c[1] = lo[1];
-      if (n + 2 < N) c[2] = hi[0];
-      if (n + 3 < N) c[3] = hi[1];
-    }
-  }
-}
-
-// One 128-deep K step of a WTM x WTN wave tile: acc[i][j] += A_i · B_jᵀ.
-template <int FM, int FN, int FA, int FB, int MODE>
-__device__ __forceinline__ void wave_kstep(const uint8_t* sa, const uint8_t* sb, int a_row0, int b_row0,
-                                           int lane, v4f (&acc)[FM][FN]) {
-  v8i bf[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) bf[j] = lds_frag(sb, b_row0 + j * 16 + (lane & 15), lane);
-  if constexpr (MODE == kAccumMfma8) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const v8i af = lds_frag(sa, a_row0 + i * 16 + (lane & 15), lane);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = mfma_fp8<FB, FA>(bf[j], af, acc[i][j]);
-    }
-  } else {
-    v8i af[FM];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) af[i] = lds_frag(sa, a_row0 + i * 16 + (lane & 15), lane);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      v8h bh[FN];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bh[j] = widen8<FB>((uint32_t)bf[j][2 * s], (uint32_t)bf[j][2 * s + 1]);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const v8h ah = widen8<FA>((uint32_t)af[i][2 * s], (uint32_t)af[i][2 * s + 1]);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bh[j], ah, acc[i][j], 0, 0, 0);
-      }
-    }
-  }
 }
 
 }  // namespace fp8mi

@@ -1,0 +1,54 @@
+"""The delayed-scaling step (fused amax+cast, history update) captured in a HIP
+graph: every replay must match the same step run eagerly, with eager work and
+synchronisations between replays (graph memory nodes are not used by the
+path, and the cast's reduction goes through a workspace, not cleared memory)."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_precision_numerics_amd as fm
+from gpu_helpers import announce, device
+
+pytestmark = pytest.mark.gpu
+
+
+def _state_arrays(st):
+    return {k: getattr(st, k).detach().cpu().numpy().copy() for k in ("history", "head", "scale", "scale_inv", "amax", "sat")}
+
+
+def test_graph_replays_match_eager_delayed_scaling():
+    dev = device()
+    rng = np.random.default_rng(77)
+    xs = [torch.from_numpy((rng.standard_normal((512, 1024)) * 3.0 ** t).astype(np.float32)).to(dev).to(torch.bfloat16)
+          for t in range(4)]
+    q_eager = torch.empty((512, 1024), dtype=torch.uint8, device=dev)
+    q_graph = torch.empty_like(q_eager)
+    eager = fm.DelayedScalingState("e4m3", 16, device=dev)
+    st = fm.DelayedScalingState("e4m3", 16, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        warm = fm.DelayedScalingState("e4m3", 16, device=dev)
+        warm.quantize(xs[0], q=q_graph, count_saturation=True)
+        warm.update()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for x in xs:
+            st.quantize(x, q=q_graph, count_saturation=True)
+            st.update()
+    for replay in range(3):
+        announce(f"graph replay {replay}")
+        graph.replay()
+        for x in xs:                       # the same four steps, eagerly
+            eager.quantize(x, q=q_eager, count_saturation=True)
+            eager.update()
+        torch.cuda.synchronize()
+        a, b = _state_arrays(st), _state_arrays(eager)
+        for k in a:
+            assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), (replay, k)
+        assert torch.equal(q_graph, q_eager)
+        # unrelated eager work on the stream between replays
+        torch.zeros(1 << 20, device=dev).add_(1.0).sum().item()
