@@ -54,6 +54,57 @@ __device__ __forceinline__ void dma_lds16(__amdgpu_buffer_rsrc_t r, uint32_t lds
 // The next stage's loads are issued in this many groups within a step.
 constexpr int kDmaGroups = 4;
 
+// The operand slabs of one output tile: rows [m0, m_end) of A and [n0, n_end)
+// of B, both row-major with K bytes per row, fetched 128 K bytes per step.
+// Direct loads: load q of wave w fills tile rows (w + q*NW)*8 .. +7; lane i
+// fills position i & 7 of row i >> 3 of that group with the granule stored
+// there under the swizzle (which depends on the row's low 4 bits only, i.e. not
+// on q since NW is even).  One buffer resource per operand covers its rows
+// from the tile start to the edge, so rows past the edge read as zero without
+// touching memory.
+template <int BM, int BN, int NW>
+struct SlabLoader {
+  static constexpr int LQA = BM / 8 / NW, LQB = BN / 8 / NW;  // direct-load instructions per wave per step
+  static constexpr int PER = (LQA + LQB + kDmaGroups - 1) / kDmaGroups;
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows must split evenly over the wavefronts");
+  static_assert(NW % 2 == 0, "the swizzle of a lane's load must not depend on its row group");
+  const uint8_t* A;
+  const uint8_t* B;
+  int64_t m0, m_end, n0, n_end;
+  int K, w, voff;
+  __amdgpu_buffer_rsrc_t ra, rb;
+
+  __device__ __forceinline__ SlabLoader(const uint8_t* A_, int64_t m0_, int64_t m_end_, const uint8_t* B_,
+                                        int64_t n0_, int64_t n_end_, int K_, int w_, int lane)
+      : A(A_), B(B_), m0(m0_), m_end(m_end_), n0(n0_), n_end(n_end_), K(K_), w(w_) {
+    ra = operand_rsrc(A + m0 * K, m_end - m0, K);
+    rb = operand_rsrc(B + n0 * K, n_end - n0, K);
+    const int lrow = w * 8 + (lane >> 3);
+    voff = lrow * K + (((lane & 7) ^ lds_swz(lrow)) & 7) * 16;
+  }
+  // Group g of the loads of step kt into the stage at `dst`: loads
+  // d = g*PER .. of the wave's LQA + LQB (A first).  A group is pinned where it
+  // is issued.
+  __device__ __forceinline__ void issue(uint8_t* dst, int kt, int g) const {
+    const int k0 = kt * kBK;
+    const uint32_t la = lds_addr(dst) + w * 1024, lb = lds_addr(dst + BM * kBK) + w * 1024;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int d = g * PER + e;
+      if (d >= LQA + LQB) break;
+      if (d < LQA) dma_lds16(ra, la + d * NW * 1024, voff, d * NW * 8 * K + k0);
+      else dma_lds16(rb, lb + (d - LQA) * NW * 1024, voff, (d - LQA) * NW * 8 * K + k0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // A ragged last K step, zero-filled through registers (all threads of the workgroup).
+  __device__ __forceinline__ void ragged(uint8_t* dst, int kt, int t) const {
+    tile_load_zero_fill<BM, 64 * NW>(A, K, m0, m_end, kt * kBK, K, dst, t);
+    tile_load_zero_fill<BN, 64 * NW>(B, K, n0, n_end, kt * kBK, K, dst + BM * kBK, t);
+  }
+};
+
 // The K loop shared by both accumulation modes.  `step` handles one full step
 // whose successor is also full: load step kt+1 into `nxt` while contracting
 // `cur`.  Two steps per iteration keep each stage pointer fixed at compile
@@ -186,10 +237,7 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
   // Output block of one matrix-core instruction: 16x16 (FP8 path), 32x32 (fp16 path).
   constexpr int BLK = MODE == kAccumMfma8 ? 16 : 32;
   constexpr int FM = WTM / BLK, FN = WTN / BLK;
-  constexpr int LQA = BM / 8 / NW, LQB = BN / 8 / NW;  // direct-load instructions per wave per step
   static_assert(FM >= 1 && FN >= 1 && WTM % BLK == 0 && WTN % BLK == 0, "wave tile shape");
-  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows must split evenly over the wavefronts");
-  static_assert(NW % 2 == 0, "the swizzle of a lane's load must not depend on its row group");
   constexpr int STAGE = (BM + BN) * kBK;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
@@ -202,36 +250,9 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
   const int nk = (K + kBK - 1) / kBK;
   const bool ragged_k = (K % kBK) != 0;
 
-  // Direct loads: load q of wave w fills tile rows (w + q*NW)*8 .. +7; lane i
-  // fills position i & 7 of row i >> 3 of that group with the granule stored
-  // there under the swizzle (which depends on the row's low 4 bits only, i.e.
-  // not on q since NW is even).
-  const __amdgpu_buffer_rsrc_t ra = operand_rsrc(A + m_base * K, M - m_base, K);
-  const __amdgpu_buffer_rsrc_t rb = operand_rsrc(B + n_base * K, N - n_base, K);
-  const int lrow = w * 8 + (lane >> 3);
-  const int voff = lrow * K + (((lane & 7) ^ lds_swz(lrow)) & 7) * 16;
-  // Group g of the loads of step kt into stage `dst`: loads d = g*PER .. of the
-  // wave's LQA + LQB (A first).  A group is pinned where it is issued.
-  auto issue_direct = [&](uint8_t* dst, int kt, int g) {
-    constexpr int PER = (LQA + LQB + kDmaGroups - 1) / kDmaGroups;
-    const int k0 = kt * kBK;
-    const uint32_t la = lds_addr(dst) + w * 1024, lb = lds_addr(dst + BM * kBK) + w * 1024;
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int d = g * PER + e;
-      if (d >= LQA + LQB) break;
-      if (d < LQA) dma_lds16(ra, la + d * NW * 1024, voff, d * NW * 8 * K + k0);
-      else dma_lds16(rb, lb + (d - LQA) * NW * 1024, voff, (d - LQA) * NW * 8 * K + k0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // Zero-filled register path for a ragged last K step.
-  auto stage_ragged = [&](int kt, int stage) {
-    uint8_t* sa = smem + stage * STAGE;
-    tile_load_zero_fill<BM, NT>(A, K, m_base, M, kt * kBK, K, sa, t);
-    tile_load_zero_fill<BN, NT>(B, K, n_base, N, kt * kBK, K, sa + BM * kBK, t);
-  };
+  const SlabLoader<BM, BN, NW> slabs(A, m_base, M, B, n_base, N, K, w, lane);
+  auto issue_direct = [&](uint8_t* dst, int kt, int g) { slabs.issue(dst, kt, g); };
+  auto stage_ragged = [&](int kt, int stage) { slabs.ragged(smem + stage * STAGE, kt, t); };
 
   // Fragment reads.  FP8 path (16x16x128): lane l takes row l & 15 of a
   // 16-row block and the 32-byte K slice l >> 4 (granules 2h, 2h+1).  fp16

@@ -11,65 +11,223 @@
 // accumulator as
 //     acc += P * (sinv_a[m][kb] * sinv_b[g][n/128][kb]),
 // so every 1x128 activation tile and 128x128 weight block keeps its own scale.
-// The tile scheduler finds each workgroup's expert from the device-side row
-// offsets, so the host never needs the token counts.
+// Output tiles are laid end to end over the experts' row ranges; each
+// workgroup finds its expert from the device-side row offsets, so the host
+// never needs the token counts.
 //
-// Layout and data movement follow the dense kernel (gemm_kernel.hpp): 128x128
-// output tiles, 4 wavefronts of 64x64, two LDS stages filled by buffer loads
-// issued one step ahead (rows past the expert's last row fall outside the
-// buffer resource and are never stored), the measured LDS swizzle, and the
-// output tile written through LDS as whole rows.  Two workgroups share a CU.
+// Both kernels use the dense kernel's data movement (gemm_kernel.hpp): two LDS
+// stages filled by buffer loads issued one step ahead (rows past the expert's
+// last row fall outside the buffer resource and are never stored), the
+// measured LDS swizzle, and the output tile written through LDS as whole rows.
+//
+// * FP8 matrix-core mode: one V_MFMA_F32_16X16X128_F8F6F4 covers a whole
+//   128-deep step of a 16x16 block, so its result IS the partial P and is
+//   promoted right away; only the running accumulators stay live.  That allows
+//   the dense kernel's wave tile (64x128, A fragments resident, B streamed) in
+//   128x512 workgroup tiles: 128 rows because token counts come in multiples of
+//   128, 512 columns so that each wave's 128 columns meet one weight block.
+// * exact mode: the 16-deep fp16 instructions build P over eight sub-steps, so
+//   P and the accumulator are both live; 128x128 tiles of four 64x64 waves,
+//   two workgroups per CU.
 #include "gemm_kernel.hpp"
 #include "launch.hpp"
 
 namespace fp8mi {
 namespace {
 
-template <int BM, int BN, int WM, int WN, int OUT, int MODE>
-__global__ __launch_bounds__(64 * WM* WN) void grouped_gemm_kernel(
+constexpr int kSchedValu = 0x002;
+
+// Output tiles of BM rows are laid end to end over the experts' row intervals
+// [m_offsets[g], m_offsets[g+1]) (made non-decreasing and clamped to
+// [0, total_m]).  Finds the expert of M tile `mt` and the tile's first row and
+// the expert's end row; false if `mt` lies past the last expert's tiles.  The
+// arguments are uniform over the workgroup, so this runs on the scalar unit.
+template <int BM>
+__device__ __forceinline__ bool expert_tile(const int32_t* __restrict__ m_offsets, int G, int total_m, int mt,
+                                            int* g_out, int64_t* row0, int64_t* row_end) {
+  int acc_tiles = 0, prev = 0;
+  for (int g = 0; g < G; ++g) {
+    int lo = m_offsets[g], hi = m_offsets[g + 1];
+    lo = lo < prev ? prev : (lo > total_m ? total_m : lo);
+    hi = hi < lo ? lo : (hi > total_m ? total_m : hi);
+    prev = hi;
+    const int tiles = (hi - lo + BM - 1) / BM;
+    if (mt < acc_tiles + tiles) {
+      *g_out = g;
+      *row0 = lo + (int64_t)(mt - acc_tiles) * BM;
+      *row_end = hi;
+      return true;
+    }
+    acc_tiles += tiles;
+  }
+  return false;
+}
+
+// Rows of one output pass through the LDS: the largest power of two that fits
+// `bytes` and divides the tile.
+template <int BM>
+constexpr int pass_rows(int bytes, int row_bytes) {
+  int p = BM;
+  while (p > 1 && p * row_bytes > bytes) p >>= 1;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// FP8 matrix-core mode.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int OUT>
+__global__ __launch_bounds__(64 * WM* WN) void grouped_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sinv_a, const uint8_t* __restrict__ B,
     const float* __restrict__ sinv_b, const int32_t* __restrict__ m_offsets, int G, int total_m,
     int N, int K, void* __restrict__ C, int tiles_n) {
   constexpr int NW = WM * WN, NT = 64 * NW;
   constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int BLK = MODE == kAccumMfma8 ? 16 : 32;
-  constexpr int FM = WTM / BLK, FN = WTN / BLK;
-  constexpr int LQA = BM / 8 / NW, LQB = BN / 8 / NW;
-  static_assert(FM >= 1 && FN >= 1 && WTM % BLK == 0 && WTN % BLK == 0 && WTN <= 128, "wave tile shape");
-  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0 && NW % 2 == 0, "load split");
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  static_assert(WTM % 16 == 0 && WTN == 128, "a wave's columns must be one 128-wide weight block");
+  static_assert(FN >= kDmaGroups, "one load group per leading B block");
   constexpr int STAGE = (BM + BN) * kBK;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
-  __shared__ int s_info[3];
 
+  // Consecutive workgroups walk the N tiles of one M tile; the round-robin
+  // deal of workgroups to XCDs then gives each XCD a fixed set of columns.
   const int tn = blockIdx.x % tiles_n, mt = blockIdx.x / tiles_n;
+  int gidx;
+  int64_t row0, row_end;
+  if (!expert_tile<BM>(m_offsets, G, total_m, mt, &gidx, &row0, &row_end)) return;  // uniform exit
+
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  if (t == 0) {
-    // Expert intervals [lo, hi) made non-decreasing and clamped to [0, total_m].
-    int acc_tiles = 0, prev = 0, found = -1, row0 = 0, row_end = 0;
-    for (int g = 0; g < G; ++g) {
-      int lo = m_offsets[g], hi = m_offsets[g + 1];
-      lo = lo < prev ? prev : (lo > total_m ? total_m : lo);
-      hi = hi < lo ? lo : (hi > total_m ? total_m : hi);
-      prev = hi;
-      const int tiles = (hi - lo + BM - 1) / BM;
-      if (mt < acc_tiles + tiles) {
-        found = g;
-        row0 = lo + (mt - acc_tiles) * BM;
-        row_end = hi;
-        break;
-      }
-      acc_tiles += tiles;
-    }
-    s_info[0] = found;
-    s_info[1] = row0;
-    s_info[2] = row_end;
-  }
-  __syncthreads();
-  const int gidx = s_info[0];
-  if (gidx < 0) return;  // workgroup beyond the last expert's tiles (uniform exit)
-  const int64_t row0 = s_info[1], row_end = s_info[2];
+  const int wm = w / WN, wn = w % WN;
+  const int64_t n_base = (int64_t)tn * BN;
+  const int nk = (K + kBK - 1) / kBK, nfull = K / kBK;
+  const bool ragged_k = (K % kBK) != 0;
+  const int nbn = (N + 127) / 128;
+  const uint8_t* Bg = B + (int64_t)gidx * N * K;
 
+  const SlabLoader<BM, BN, NW> slabs(A, row0, row_end, Bg, n_base, N, K, w, lane);
+  auto issue_direct = [&](uint8_t* dst, int kt, int g) { slabs.issue(dst, kt, g); };
+  auto stage_ragged = [&](int kt, int stage) { slabs.ragged(smem + stage * STAGE, kt, t); };
+
+  // 16x16x128 fragments: lane l takes row l & 15 of a 16-row block and the
+  // 32-byte K slice l >> 4 (granules 2h, 2h+1).
+  const int rr = lane & 15, hh = lane >> 4;
+  const int swz = lds_swz(rr);
+  auto frag = [&](const uint8_t* tile, int r0) {
+    const uint8_t* p = tile + (r0 + rr) * kBK;
+    const uint4 lo = *reinterpret_cast<const uint4*>(p + (((2 * hh) ^ swz) & 7) * 16);
+    const uint4 hi = *reinterpret_cast<const uint4*>(p + (((2 * hh + 1) ^ swz) & 7) * 16);
+    return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+
+  // Block scales of the lane's output row in each A block (the row clamped
+  // inside the expert) and of the wave's weight block, one step ahead: the
+  // values of step kt+1 are loaded while step kt runs.
+  uint32_t sa_off[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t r = row0 + wm * WTM + i * 16 + rr;
+    sa_off[i] = (uint32_t)((r < row_end ? r : row0) * nk);
+  }
+  const int nb = (int)((n_base + wn * WTN) >> 7);
+  const float* sb_blk = sinv_b + ((int64_t)gidx * nbn + (nb < nbn ? nb : nbn - 1)) * nk;
+  float sa_n[FM], sb_n;
+  auto load_scales = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) sa_n[i] = sinv_a[sa_off[i] + kt];
+    sb_n = sb_blk[kt];
+  };
+  load_scales(0);
+  int kstep = 0;
+
+  v4f acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  v8i af[FM], bf[2];
+  auto load_frags = [&](const uint8_t* st) {
+    bf[0] = frag(st + BM * kBK, wn * WTN);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[i] = frag(st, wm * WTM + i * 16);
+  };
+  // One step.  Each MFMA's partial is promoted after the next MFMA has been
+  // issued, so the promotion does not wait for the product it consumes.
+  auto compute = [&](const uint8_t* st, auto&& dma) {
+    float s[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) s[i] = sa_n[i] * sb_n;
+    ++kstep;
+    load_scales(kstep < nk ? kstep : nk - 1);
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    v4f p[2];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      if (j < kDmaGroups) dma(j);
+      if (j + 1 < FN) bf[(j + 1) & 1] = frag(st + BM * kBK, wn * WTN + (j + 1) * 16);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int c = j * FM + i;
+        p[c & 1] = mfma_fp8<kE4M3, kE4M3>(bf[j & 1], af[i], zero);
+        if (c > 0) {
+          const int jp = (c - 1) / FM, ip = (c - 1) % FM;
+          acc[ip][jp] += p[(c - 1) & 1] * s[ip];
+        }
+      }
+    }
+    acc[FM - 1][FN - 1] += p[(FM * FN - 1) & 1] * s[FM - 1];
+  };
+  auto interleave = [&]() {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, FM, 0);
+    }
+  };
+  run_main_loop(smem, smem + STAGE, nfull, nk, ragged_k, issue_direct, stage_ragged, load_frags, compute,
+                interleave);
+
+  // Lane l holds row m = l & 15 of each 16x16 block (the A operand went
+  // second) and columns n = 4(l >> 4) .. +3; rows past the expert are not stored.
+  using TW = TileWriter<OUT, BM, BN, NT>;
+  constexpr int PASS = pass_rows<BM>(2 * STAGE, TW::ROWB);
+  TW tw{smem, PASS};
+#pragma unroll 1
+  for (int r0 = 0; r0 < BM; r0 += PASS) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WTM + i * 16 + rr;
+      if (r < r0 || r >= r0 + PASS) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) tw.put(r - r0, wn * WTN + j * 16 + 4 * hh, acc[i][j]);
+    }
+    __syncthreads();
+    tw.flush(C, row_end, N, row0 + r0, n_base, t);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Exact mode (FP8 widened to fp16, 32x32x16 instructions).
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int OUT>
+__global__ __launch_bounds__(64 * WM* WN) void grouped_exact_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sinv_a, const uint8_t* __restrict__ B,
+    const float* __restrict__ sinv_b, const int32_t* __restrict__ m_offsets, int G, int total_m,
+    int N, int K, void* __restrict__ C, int tiles_n) {
+  constexpr int NW = WM * WN, NT = 64 * NW;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0 && WTN <= 128, "wave tile shape");
+  constexpr int STAGE = (BM + BN) * kBK;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+
+  const int tn = blockIdx.x % tiles_n, mt = blockIdx.x / tiles_n;
+  int gidx;
+  int64_t row0, row_end;
+  if (!expert_tile<BM>(m_offsets, G, total_m, mt, &gidx, &row0, &row_end)) return;  // uniform exit
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w / WN, wn = w % WN;
   const int64_t n_base = (int64_t)tn * BN;
   const int nk = (K + kBK - 1) / kBK, nfull = K / kBK;
@@ -77,29 +235,23 @@ __global__ __launch_bounds__(64 * WM* WN) void grouped_gemm_kernel(
   const uint8_t* Bg = B + (int64_t)gidx * N * K;
   const float* sbg = sinv_b + (int64_t)gidx * nbn * nk;
 
-  // Operand slabs: buffer resources over this expert's rows of A and of B_g.
-  const __amdgpu_buffer_rsrc_t ra = operand_rsrc(A + row0 * K, row_end - row0, K);
-  const __amdgpu_buffer_rsrc_t rb = operand_rsrc(Bg + n_base * K, N - n_base, K);
-  const int lrow = w * 8 + (lane >> 3);
-  const int voff = lrow * K + (((lane & 7) ^ lds_swz(lrow)) & 7) * 16;
+  const SlabLoader<BM, BN, NW> slabs(A, row0, row_end, Bg, n_base, N, K, w, lane);
   auto fill = [&](uint8_t* st, int kt) {
     if (kt < nfull) {
-      const int k0 = kt * kBK;
-      const uint32_t la = lds_addr(st) + w * 1024, lb = lds_addr(st + BM * kBK) + w * 1024;
 #pragma unroll
-      for (int q = 0; q < LQA; ++q) dma_lds16(ra, la + q * NW * 1024, voff, q * NW * 8 * K + k0);
-#pragma unroll
-      for (int q = 0; q < LQB; ++q) dma_lds16(rb, lb + q * NW * 1024, voff, q * NW * 8 * K + k0);
-    } else {  // ragged last K step: zero-filled through registers
-      tile_load_zero_fill<BM, NT>(A, K, row0, row_end, kt * kBK, K, st, t);
-      tile_load_zero_fill<BN, NT>(Bg, K, n_base, N, kt * kBK, K, st + BM * kBK, t);
+      for (int g = 0; g < kDmaGroups; ++g) slabs.issue(st, kt, g);
+    } else {
+      slabs.ragged(st, kt, t);
     }
   };
 
-  const int rr = lane & (BLK - 1), hh = lane / BLK;
+  // 32x32x16 fragments (eight K sub-steps of 16): lane l takes row l & 31 of a
+  // 32-row block and the 64-byte half l >> 5 of the step (granules 4h..4h+3);
+  // sub-step s uses bytes [8s, 8s+8) of it, for both operands alike.
+  const int rr = lane & 31, hh = lane >> 5;
   const int swz = lds_swz(rr);
-  auto granule = [&](const uint8_t* tile, int row0_, int g) {
-    return *reinterpret_cast<const uint4*>(tile + (row0_ + rr) * kBK + (((g ^ swz) & 7) << 4));
+  auto granule = [&](const uint8_t* tile, int r0, int g) {
+    return *reinterpret_cast<const uint4*>(tile + (r0 + rr) * kBK + (((g ^ swz) & 7) << 4));
   };
 
   // Scale lookups: the lane's row in each A block (clamped inside the expert),
@@ -107,22 +259,21 @@ __global__ __launch_bounds__(64 * WM* WN) void grouped_gemm_kernel(
   int64_t arow[FM];
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int64_t r = row0 + wm * WTM + i * BLK + rr;
+    const int64_t r = row0 + wm * WTM + i * 32 + rr;
     arow[i] = r < row_end ? r : row0;
   }
   int bblk[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
-    const int nb = (int)((n_base + wn * WTN + j * BLK) / 128);
+    const int nb = (int)((n_base + wn * WTN + j * 32) / 128);
     bblk[j] = nb < nbn ? nb : nbn - 1;
   }
 
-  using Acc = typename std::conditional<MODE == kAccumMfma8, v4f, v16f>::type;
-  Acc acc[FM][FN];
+  v16f acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = Acc{};
+    for (int j = 0; j < FN; ++j) acc[i][j] = (v16f){};
 
   uint8_t* const s0 = smem;
   uint8_t* const s1 = smem + STAGE;
@@ -139,51 +290,34 @@ __global__ __launch_bounds__(64 * WM* WN) void grouped_gemm_kernel(
     for (int j = 0; j < FN; ++j) sb_v[j] = sbg[bblk[j] * nk + kt];
     if (kt + 1 < nk) fill(nxt, kt + 1);
     __builtin_amdgcn_sched_barrier(0);
-    Acc part[FM][FN];
+    v16f part[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) part[i][j] = Acc{};
-    if constexpr (MODE == kAccumMfma8) {
-      v8i af[FM];
+      for (int j = 0; j < FN; ++j) part[i][j] = (v16f){};
+    uint4 ar[FM][4], br[FN][4];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const uint4 lo = granule(cur, wm * WTM + i * 16, 2 * hh), hi = granule(cur, wm * WTM + i * 16, 2 * hh + 1);
-        af[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) ar[i][c] = granule(cur, wm * WTM + i * 32, 4 * hh + c);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) br[j][c] = granule(cur + BM * kBK, wn * WTN + j * 32, 4 * hh + c);
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      v8h bh[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const uint8_t* tb = cur + BM * kBK;
-        const uint4 lo = granule(tb, wn * WTN + j * 16, 2 * hh), hi = granule(tb, wn * WTN + j * 16, 2 * hh + 1);
-        const v8i bf = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-#pragma unroll
-        for (int i = 0; i < FM; ++i) part[i][j] = mfma_fp8<kE4M3, kE4M3>(bf, af[i], part[i][j]);
-      }
-    } else {
-      uint4 ar[FM][4], br[FN][4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) ar[i][c] = granule(cur, wm * WTM + i * 32, 4 * hh + c);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) br[j][c] = granule(cur + BM * kBK, wn * WTN + j * 32, 4 * hh + c);
+        const uint4 g = br[j][s >> 1];
+        bh[j] = (s & 1) ? widen8<kE4M3>(g.z, g.w) : widen8<kE4M3>(g.x, g.y);
       }
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        v8h bh[FN];
+      for (int i = 0; i < FM; ++i) {
+        const uint4 g = ar[i][s >> 1];
+        const v8h ah = (s & 1) ? widen8<kE4M3>(g.z, g.w) : widen8<kE4M3>(g.x, g.y);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const uint4 g = br[j][s >> 1];
-          bh[j] = (s & 1) ? widen8<kE4M3>(g.z, g.w) : widen8<kE4M3>(g.x, g.y);
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const uint4 g = ar[i][s >> 1];
-          const v8h ah = (s & 1) ? widen8<kE4M3>(g.z, g.w) : widen8<kE4M3>(g.x, g.y);
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bh[j], ah, part[i][j], 0, 0, 0);
-        }
+        for (int j = 0; j < FN; ++j)
+          part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bh[j], ah, part[i][j], 0, 0, 0);
       }
     }
     // Promotion of this 128-deep partial with its block scales.
@@ -195,45 +329,58 @@ __global__ __launch_bounds__(64 * WM* WN) void grouped_gemm_kernel(
     wait_loads_and_barrier();
   }
 
-  // Output tile through LDS, whole rows; rows past the expert are not stored.
+  // Lane l holds row m = l & 31 of each 32x32 block and columns
+  // n = 8g + 4(l >> 5) + 0..3 in registers 4g..4g+3; rows past the expert are
+  // not stored.
   using TW = TileWriter<OUT, BM, BN, NT>;
-  constexpr int PASS = (2 * STAGE / TW::ROWB) < BM ? (2 * STAGE / TW::ROWB) : BM;
-  static_assert(BM % PASS == 0, "output passes must tile the rows");
+  constexpr int PASS = pass_rows<BM>(2 * STAGE, TW::ROWB);
   TW tw{smem, PASS};
 #pragma unroll 1
   for (int r0 = 0; r0 < BM; r0 += PASS) {
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int r = wm * WTM + i * BLK + rr;
+      const int r = wm * WTM + i * 32 + rr;
       if (r < r0 || r >= r0 + PASS) continue;
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        if constexpr (MODE == kAccumMfma8) {
-          tw.put(r - r0, wn * WTN + j * 16 + 4 * (lane >> 4), acc[i][j]);
-        } else {
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const v4f v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-            tw.put(r - r0, wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5), v);
-          }
+        for (int g = 0; g < 4; ++g) {
+          const v4f v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          tw.put(r - r0, wn * WTN + j * 32 + 8 * g + 4 * hh, v);
         }
-      }
     }
     __syncthreads();
     tw.flush(C, row_end, N, row0 + r0, n_base, t);
   }
 }
 
-template <int BM, int BN, int WM, int WN, int OUT, int MODE>
-hipError_t run(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
-               const int32_t* offs, int G, int64_t total_m, int64_t N, int64_t K, void* C,
-               hipStream_t st) {
-  const int tiles_n = (int)((N + BN - 1) / BN);
-  const int64_t tiles_m = (total_m + BM - 1) / BM + G;  // upper bound over any split into G experts
-  hipLaunchKernelGGL((grouped_gemm_kernel<BM, BN, WM, WN, OUT, MODE>), dim3((unsigned)(tiles_m * tiles_n)),
-                     dim3(64 * WM * WN), 0, st, A, sa, B, sb, offs, G, (int)total_m, (int)N, (int)K, C,
-                     tiles_n);
+// Grid: N tiles times an upper bound on the M tiles over any split of total_m
+// rows into G experts (each expert adds at most one partial tile).
+template <int BM, int BN>
+dim3 grouped_grid(int64_t total_m, int G, int64_t N, int* tiles_n) {
+  *tiles_n = (int)((N + BN - 1) / BN);
+  const int64_t tiles_m = (total_m + BM - 1) / BM + G;
+  return dim3((unsigned)(tiles_m * *tiles_n));
+}
+
+template <int BM, int BN, int WM, int WN, int OUT>
+hipError_t run_fp8(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb, const int32_t* offs,
+                   int G, int64_t total_m, int64_t N, int64_t K, void* C, hipStream_t st) {
+  int tiles_n;
+  const dim3 grid = grouped_grid<BM, BN>(total_m, G, N, &tiles_n);
+  hipLaunchKernelGGL((grouped_fp8_kernel<BM, BN, WM, WN, OUT>), grid, dim3(64 * WM * WN), 0, st, A, sa, B, sb,
+                     offs, G, (int)total_m, (int)N, (int)K, C, tiles_n);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int OUT>
+hipError_t run_exact(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb, const int32_t* offs,
+                     int G, int64_t total_m, int64_t N, int64_t K, void* C, hipStream_t st) {
+  int tiles_n;
+  const dim3 grid = grouped_grid<BM, BN>(total_m, G, N, &tiles_n);
+  hipLaunchKernelGGL((grouped_exact_kernel<BM, BN, WM, WN, OUT>), grid, dim3(64 * WM * WN), 0, st, A, sa, B, sb,
+                     offs, G, (int)total_m, (int)N, (int)K, C, tiles_n);
   return hipGetLastError();
 }
 
@@ -246,12 +393,12 @@ hipError_t launch_grouped_gemm(const uint8_t* A, const float* sinv_a, const uint
   if (total_m == 0 || N == 0) return hipSuccess;
   if (accum == kAccumMfma8) {
     if (ctype == kBF16)
-      return run<128, 128, 2, 2, kBF16, kAccumMfma8>(A, sinv_a, B, sinv_b, m_offsets, G, total_m, N, K, C, stream);
-    return run<128, 128, 2, 2, kF32, kAccumMfma8>(A, sinv_a, B, sinv_b, m_offsets, G, total_m, N, K, C, stream);
+      return run_fp8<128, 512, 2, 4, kBF16>(A, sinv_a, B, sinv_b, m_offsets, G, total_m, N, K, C, stream);
+    return run_fp8<128, 512, 2, 4, kF32>(A, sinv_a, B, sinv_b, m_offsets, G, total_m, N, K, C, stream);
   }
   if (ctype == kBF16)
-    return run<128, 128, 2, 2, kBF16, kAccumExact>(A, sinv_a, B, sinv_b, m_offsets, G, total_m, N, K, C, stream);
-  return run<128, 128, 2, 2, kF32, kAccumExact>(A, sinv_a, B, sinv_b, m_offsets, G, total_m, N, K, C, stream);
+    return run_exact<128, 128, 2, 2, kBF16>(A, sinv_a, B, sinv_b, m_offsets, G, total_m, N, K, C, stream);
+  return run_exact<128, 128, 2, 2, kF32>(A, sinv_a, B, sinv_b, m_offsets, G, total_m, N, K, C, stream);
 }
 
 }  // namespace fp8mi
