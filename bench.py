@@ -13,8 +13,9 @@ Inputs are synthetic (seeded), resident in HBM before timing starts.
 Printed on stdout: ONE JSON line.  `value` is GEMM FLOP / step time (TFLOP/s
 of the whole step); `roofline` is the GEMM kernel alone (HIP events around
 each launch on its stream); `extra` holds the delayed-scaling stream
-(32 x 8192x4096, HBM GB/s of the fused amax+cast), the HYBRID dgrad GEMM and
-the fine-grained MoE grouped GEMM; `cpu_baseline` times the CPU oracle on a
+(32 x 8192x4096, HBM GB/s of the fused amax+cast), one HYBRID linear-layer
+training step at the FC1 shape (forward, dgrad, wgrad, each launch timed), the
+fine-grained MoE grouped GEMM and the vendor library's GEMMs on the FC1 shape; `cpu_baseline` times the CPU oracle on a
 bounded slice of the same step.
 """
 
@@ -267,42 +268,68 @@ def stream_bench(torch, fm, dtype, passes=3):
             "algorithmic_bytes_per_step": bytes_per_step, "per_step": per_step}
 
 
-def dgrad_bench(torch, fm, iters=20):
-    from synth import dgrad_hybrid
+def linear_bench(torch, fm, iters=10):
+    """One FP8 linear layer training step at the FC1 shape (tokens 8192, in 4096,
+    out 16384) under HYBRID delayed scaling: forward (cast-transpose of X and W,
+    Y = X W^T bf16), backward (cast-transpose of dY to E5M2, dX = dY W and
+    dW = dY^T X in fp32), the three history updates.  Each launch is timed on its
+    own, and the whole step once more as one region."""
+    from synth import dgrad_hybrid, fc1_forward
 
     dev = torch.device("cuda:0")
-    M, K, N = 8192, 16384, 4096
-    log("generating dgrad inputs ...")
-    d = dgrad_hybrid(M, K, N, priors=False)
+    T, I, O = 8192, 4096, 16384
+    log("generating linear-layer inputs ...")
+    d = dgrad_hybrid(T, O, I, priors=False)
     G = torch.from_numpy(d["dY"].data.view("int16")).to(dev).view(torch.bfloat16)
-    W = torch.from_numpy(d["W"].data.view("int16")).to(dev).view(torch.bfloat16)
+    W = torch.from_numpy(d["W"].data.view("int16")).to(dev).view(torch.bfloat16)      # [out x in]
     del d
-    stG = fm.DelayedScalingState("e5m2", 16, device=dev)
-    stW = fm.DelayedScalingState("e4m3", 16, device=dev)
-    qg = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    qwT = torch.empty((N, K), dtype=torch.uint8, device=dev)
-    for _ in range(2):                    # second pass casts with the amax-derived scale
-        stG.quantize(G, q=qg)
-        stG.update()
-        stW.quantize(W, q_t=qwT)
-        stW.update()
-    c = torch.empty((M, N), dtype=torch.float32, device=dev)
-    flops = 2.0 * M * N * K
+    X = torch.from_numpy(fc1_forward(T, I, O, priors=False)["X"].data.view("int16")).to(dev).view(torch.bfloat16)
+    Y = torch.empty((T, O), dtype=torch.bfloat16, device=dev)
+    dX = torch.empty((T, I), dtype=torch.float32, device=dev)
+    dW = torch.empty((O, I), dtype=torch.float32, device=dev)
+    flops = 2.0 * T * I * O
     res = {}
     for accum in ("exact", "mfma_fp8"):
-        timer = EventTimer(torch)
-        for i in range(iters + 3):
-            if i < 3:
-                fm.fp8_gemm(qg, "e5m2", qwT, "e4m3", stG.scale_inv, stW.scale_inv, c, accum=accum)
-            else:
-                with timer:
-                    fm.fp8_gemm(qg, "e5m2", qwT, "e4m3", stG.scale_inv, stW.scale_inv, c, accum=accum)
+        layer = fm.Fp8Linear(T, I, O, accum=accum, device=dev)
+        for _ in range(2):                    # the second step casts with amax-derived scales
+            layer.forward(X, W, Y)
+            layer.backward(G, dX, dW)
+            layer.update()
+        parts = {k: EventTimer(torch) for k in ("cast_x", "cast_w", "fwd_gemm", "cast_dy", "dgrad_gemm",
+                                                "wgrad_gemm", "update")}
+        whole = EventTimer(torch)
+        sx, sw, sg = layer.state_x, layer.state_w, layer.state_g
+        for _ in range(iters):
+            with parts["cast_x"]:
+                sx.quantize(X, q=layer.qx, q_t=layer.qx_t)
+            with parts["cast_w"]:
+                sw.quantize(W, q=layer.qw, q_t=layer.qw_t)
+            with parts["fwd_gemm"]:
+                fm.fp8_gemm(layer.qx, "e4m3", layer.qw, "e4m3", sx.scale_inv, sw.scale_inv, Y, accum=accum)
+            with parts["cast_dy"]:
+                sg.quantize(G, q=layer.qg, q_t=layer.qg_t)
+            with parts["dgrad_gemm"]:
+                fm.fp8_gemm(layer.qg, "e5m2", layer.qw_t, "e4m3", sg.scale_inv, sw.scale_inv, dX, accum=accum)
+            with parts["wgrad_gemm"]:
+                fm.fp8_gemm(layer.qg_t, "e5m2", layer.qx_t, "e4m3", sg.scale_inv, sx.scale_inv, dW, accum=accum)
+            with parts["update"]:
+                layer.update()
+        for _ in range(iters):
+            with whole:
+                layer.forward(X, W, Y)
+                layer.backward(G, dX, dW)
+                layer.update()
         torch.cuda.synchronize()
-        ms = statistics.mean(timer.ms())
-        log(f"dgrad E5M2xE4M3 -> fp32 ({accum}): {ms * 1e3:.1f} us = {flops / ms / 1e9:.0f} TFLOP/s")
-        res[accum] = {"us": ms * 1e3, "tflops": flops / ms / 1e9,
-                      "frac_of_its_peak": flops / ms / 1e9 / PEAK_BY_ACCUM[accum]}
-    del G, W, qg, qwT, c
+        us = {k: statistics.mean(t.ms()) * 1e3 for k, t in parts.items()}
+        step_us = statistics.mean(whole.ms()) * 1e3
+        r = {"step_us": step_us, "step_tflops": 3 * flops / step_us / 1e6, "parts_us": us}
+        for g in ("fwd_gemm", "dgrad_gemm", "wgrad_gemm"):
+            r[g.replace("_gemm", "_tflops")] = flops / us[g] / 1e6
+        log(f"linear step ({accum}): {step_us:.1f} us = {r['step_tflops']:.0f} TFLOP/s; "
+            + ", ".join(f"{k} {v:.1f}" for k, v in us.items()))
+        res[accum] = r
+        del layer
+    del G, W, X, Y, dX, dW
     torch.cuda.empty_cache()
     return res
 
@@ -462,7 +489,7 @@ def main():
         del src, dst
     if not args.quick:
         extra["stream"] = stream_bench(torch, fm, args.stream_dtype)
-        extra["dgrad"] = dgrad_bench(torch, fm)
+        extra["linear_step"] = linear_bench(torch, fm)
         extra["moe_grouped"] = moe_bench(torch, fm)
         extra["vendor_reference"] = vendor_reference(torch)
     cpu = None

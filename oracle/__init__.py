@@ -13,6 +13,8 @@ scaling  amax, the per-tensor scale rule, the delayed-scaling amax-history
          ring, the scaled cast, and per-block (current) scaling.
 gemm     dequantised GEMM in fp64, exact integer dot products, the error
          bound, and the fine-grained grouped GEMM.
+linear   one FP8 linear-layer step (forward, data and weight gradients)
+         under the HYBRID recipe with delayed scaling.
 
 Sources (the pages this follows)
 --------------------------------
@@ -30,4 +32,4 @@ Sources (the pages this follows)
 Parity status per function is listed in each module's header.
 """
 
-from . import codec, scaling, gemm  # noqa: F401
+from . import codec, scaling, gemm, linear  # noqa: F401
