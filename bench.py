@@ -41,7 +41,7 @@ PEAK_BY_ACCUM = {"exact": PEAK_FP16_TFLOPS, "mfma_fp8": PEAK_FP8_TFLOPS}
 # HBM traffic per launch of the FC1 GEMM from two counter runs (FETCH_SIZE, WRITE_SIZE), each scaled by what
 # the same counter reads for a 256 MiB device copy (profiles/gemm_fc1_8192x16384x4096_hbm_traffic.md).  Valid
 # only for the kernel sources they were taken on: GEMM_SOURCES hashed in order must give GEMM_TRAFFIC_SHA256.
-GEMM_SOURCES = ("gemm.hip", "gemm_kernel.hpp", "gemm_tile.hpp", "device_common.hpp")
+GEMM_SOURCES = ("gemm.hip", "gemm_dispatch.hpp", "gemm_kernel.hpp", "gemm_tile.hpp", "device_common.hpp")
 GEMM_TRAFFIC_SHA256 = "d5df23936693a92d78fb5874cdb0806bc7695309e33f59ae9a250679b72f2c6c"
 GEMM_TRAFFIC = {"exact": {"read_bytes": 1243211971, "write_bytes": 268780480},
                 "mfma_fp8": {"read_bytes": 1209496637, "write_bytes": 271124331}}
@@ -273,7 +273,9 @@ def linear_bench(torch, fm, iters=10):
     out 16384) under HYBRID delayed scaling: forward (cast-transpose of X and W,
     Y = X W^T bf16), backward (cast-transpose of dY to E5M2, dX = dY W and
     dW = dY^T X in fp32), the three history updates.  Each launch is timed on its
-    own, and the whole step once more as one region."""
+    own, and the whole step once more as one region.  Also timed: the forward
+    GEMM with Y re-quantised to E4M3 in its epilogue, and the cast of the bf16 Y
+    that the unfused path would need instead."""
     from synth import dgrad_hybrid, fc1_forward
 
     dev = torch.device("cuda:0")
@@ -319,6 +321,20 @@ def linear_bench(torch, fm, iters=10):
                 layer.forward(X, W, Y)
                 layer.backward(G, dX, dW)
                 layer.update()
+        # the forward with Y re-quantised to E4M3 in the GEMM epilogue, against the
+        # unfused alternative's extra pass (the cast of the bf16 Y)
+        st_y = fm.DelayedScalingState("e4m3", 16, device=dev)
+        yq = torch.empty((T, O), dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            st_y.quantize(Y, q=yq)
+            st_y.update()
+        parts["fwd_gemm_requant"], parts["cast_y"] = EventTimer(torch), EventTimer(torch)
+        for _ in range(iters):
+            with parts["fwd_gemm_requant"]:
+                fm.fp8_gemm_requant(layer.qx, "e4m3", layer.qw, "e4m3", sx.scale_inv, sw.scale_inv, "e4m3",
+                                    st_y.scale, yq, amax=st_y.amax, sat=st_y.sat, accum=accum)
+            with parts["cast_y"]:
+                st_y.quantize(Y, q=yq)
         torch.cuda.synchronize()
         us = {k: statistics.mean(t.ms()) * 1e3 for k, t in parts.items()}
         step_us = statistics.mean(whole.ms()) * 1e3

@@ -17,7 +17,7 @@ import torch
 
 __all__ = ["E4M3", "E5M2", "F32", "BF16", "ACCUM_EXACT", "ACCUM_MFMA_FP8", "QUANTIZE_WORKSPACE_BYTES", "Fp8Error", "load_library", "library_path",
            "status_string", "version", "fp8_quantize", "fp8_amax_update", "fp8_gemm",
-           "fp8_quantize_blockwise", "fp8_grouped_gemm", "EXPORTED_SYMBOLS"]
+           "fp8_quantize_blockwise", "fp8_grouped_gemm", "fp8_gemm_requant", "EXPORTED_SYMBOLS"]
 
 E4M3, E5M2 = 0, 1
 F32, BF16 = 0, 1
@@ -27,7 +27,7 @@ ACCUMS = {"exact": ACCUM_EXACT, "mfma_fp8": ACCUM_MFMA_FP8, ACCUM_EXACT: ACCUM_E
           ACCUM_MFMA_FP8: ACCUM_MFMA_FP8}
 
 EXPORTED_SYMBOLS = ("fp8mi_status_string", "fp8mi_version", "fp8_quantize", "fp8_amax_update",
-                    "fp8_gemm", "fp8_quantize_blockwise", "fp8_grouped_gemm")
+                    "fp8_gemm", "fp8_quantize_blockwise", "fp8_grouped_gemm", "fp8_gemm_requant")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -76,6 +76,9 @@ def load_library():
     lib.fp8_quantize_blockwise.restype = ctypes.c_int
     lib.fp8_grouped_gemm.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, ctypes.c_int, ctypes.c_int, vp]
     lib.fp8_grouped_gemm.restype = ctypes.c_int
+    lib.fp8_gemm_requant.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64, i64, vp, vp, ctypes.c_int, vp,
+                                     vp, vp, vp, ctypes.c_int, vp]
+    lib.fp8_gemm_requant.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -218,6 +221,30 @@ def fp8_gemm(a, fa, b, fb, sinv_a, sinv_b, c, accum="exact", stream=None) -> Non
     with torch.cuda.device(dev):
         _call("fp8_gemm", lib.fp8_gemm(_p(a), _fmt(fa), _p(b), _fmt(fb), M, N, K, _p(sinv_a), _p(sinv_b),
                                        _p(c), ctype, _accum(accum), _stream(stream)))
+
+
+def fp8_gemm_requant(a, fa, b, fb, sinv_a, sinv_b, out_fmt, out_scale, cq, amax=None, sat=None, accum="exact",
+                     stream=None) -> None:
+    """Cq[M x N] = FP8 codes (out_fmt) of fp32((A · Bᵀ) · sinv_a · sinv_b) × out_scale,
+    with the amax of the unscaled result and the saturation count (both optional)."""
+    lib = load_library()
+    dev = a.device
+    _check(a, "a", torch.uint8, None, dev)
+    _check(b, "b", torch.uint8, None, dev)
+    _check(sinv_a, "sinv_a", torch.float32, 1, dev)
+    _check(sinv_b, "sinv_b", torch.float32, 1, dev)
+    _check(out_scale, "out_scale", torch.float32, 1, dev)
+    _check(cq, "cq", torch.uint8, None, dev)
+    _check(amax, "amax", torch.float32, 1, dev)
+    _check(sat, "sat", torch.int64, 1, dev)
+    M, K = a.shape
+    N, K2 = b.shape
+    if K2 != K or tuple(cq.shape) != (M, N):
+        raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)}, cq {tuple(cq.shape)}")
+    with torch.cuda.device(dev):
+        _call("fp8_gemm_requant", lib.fp8_gemm_requant(_p(a), _fmt(fa), _p(b), _fmt(fb), M, N, K, _p(sinv_a),
+                                                       _p(sinv_b), _fmt(out_fmt), _p(out_scale), _p(cq), _p(amax),
+                                                       _p(sat), _accum(accum), _stream(stream)))
 
 
 def fp8_quantize_blockwise(x, block_rows, fmt, q, scale_inv, stream=None) -> None:

@@ -65,7 +65,7 @@ const char* fp8mi_status_string(int status) {
   }
 }
 
-int fp8mi_version(void) { return 300; }
+int fp8mi_version(void) { return 400; }
 
 int fp8_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, const float* scale,
                  uint8_t* q, uint8_t* q_t, float* amax, unsigned long long* sat, void* workspace,
@@ -116,6 +116,27 @@ int fp8_gemm(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t M, int6
   if (dev != FP8MI_OK) return dev;
   return launched(fp8mi::launch_gemm(A, fa, B, fb, M, N, K, sinv_a, sinv_b, C, ctype, accum,
                                      (hipStream_t)stream));
+}
+
+int fp8_gemm_requant(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t M, int64_t N, int64_t K,
+                     const float* sinv_a, const float* sinv_b, int out_fmt, const float* out_scale,
+                     uint8_t* Cq, float* amax, unsigned long long* sat, int accum, void* stream) {
+  if (!fmt_ok(fa) || !fmt_ok(fb) || !fmt_ok(out_fmt)) return FP8MI_ERR_FORMAT;
+  if (!accum_ok(accum)) return FP8MI_ERR_ACCUM;
+  if (M < 0 || N < 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxGemmK) return FP8MI_ERR_SHAPE;
+  if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N)) return FP8MI_ERR_SHAPE;
+  if ((K & 15) != 0) return FP8MI_ERR_ALIGN;
+  if (((M + 127) / 128) * ((N + 127) / 128) > kMaxDim) return FP8MI_ERR_SHAPE;
+  if (M > 0 && N > 0) {
+    if (!A || !B || !sinv_a || !sinv_b || !out_scale || !Cq) return FP8MI_ERR_NULL;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(Cq)) return FP8MI_ERR_ALIGN;
+  } else if (!amax && !sat) {
+    return FP8MI_OK;
+  }
+  const int dev = check_device();
+  if (dev != FP8MI_OK) return dev;
+  return launched(fp8mi::launch_gemm_requant(A, fa, B, fb, M, N, K, sinv_a, sinv_b, out_fmt, out_scale, Cq,
+                                             amax, sat, accum, (hipStream_t)stream));
 }
 
 int fp8_quantize_blockwise(const void* x, int xtype, int64_t rows, int64_t cols, int32_t block_rows,

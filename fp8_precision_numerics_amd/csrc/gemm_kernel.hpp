@@ -20,9 +20,28 @@
 // the address state to a single register.
 #pragma once
 
+#include <type_traits>
+
 #include "gemm_tile.hpp"
 
 namespace fp8mi {
+
+// Output kinds of the epilogue besides fp32 and bf16 (kF32, kBF16): FP8 codes
+// of the result re-quantised with a caller-supplied scale.
+enum : int { kOutE4M3 = 2, kOutE5M2 = 3 };
+template <int OUT>
+constexpr int out_bytes() {
+  return OUT == kF32 ? 4 : (OUT == kBF16 ? 2 : 1);
+}
+
+// Where a re-quantising epilogue sends its by-products: the scale to apply,
+// the amax of the unscaled result (as fp32 bits) and the saturation count
+// (either pointer may be null).  Unused by the fp32 / bf16 outputs.
+struct RequantArgs {
+  const float* out_scale;
+  uint32_t* amax_bits;
+  unsigned long long* sat;
+};
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;
@@ -177,12 +196,12 @@ __device__ __forceinline__ void run_main_loop(uint8_t* s0, uint8_t* s1, int nful
 // bytes, consecutive lanes consecutive addresses.  Storing straight from the
 // matrix-core layout writes 8-16 byte pieces of many rows per instruction,
 // which costs several times the output's size in memory traffic.  Tile rows
-// are BN*sizeof(out) bytes; the 16-byte granule q of row r sits at position
+// are BN*sizeof(out) bytes (1 per FP8 code); the 16-byte granule q of row r sits at position
 // q ^ (r mod min(granules per row, 32)).  A tile that does not fit the LDS goes
 // out in row passes.
 template <int OUT, int BM, int BN, int NT>
 struct TileWriter {
-  static constexpr int CB = OUT == kF32 ? 4 : 2;           // bytes per output element
+  static constexpr int CB = out_bytes<OUT>();              // bytes per output element
   static constexpr int ROWB = BN * CB;                     // bytes per tile row
   static constexpr int GR = ROWB / 16;                     // granules per row
   static constexpr int SWZ = (GR < 32 ? GR : 32) - 1;
@@ -203,6 +222,10 @@ struct TileWriter {
       *reinterpret_cast<uint2*>(p) = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
     }
   }
+  // Four FP8 codes (byte i = column n_local + i) of tile row r_local.
+  __device__ __forceinline__ void put_codes(int r_local, int n_local, uint32_t codes) const {
+    *reinterpret_cast<uint32_t*>(lds + pos(r_local, n_local)) = codes;
+  }
   // Copy rows [0, pass_rows) of the staged pass to C rows m0.. (all threads).
   __device__ __forceinline__ void flush(void* C, int64_t M, int64_t N, int64_t m0, int64_t n0, int t) const {
     const bool full_cols = n0 + BN <= N && ((N * CB) & 15) == 0;
@@ -219,19 +242,35 @@ struct TileWriter {
         const int64_t nq = n0 + q * (16 / CB);
         for (int e = 0; e < 16 / CB; ++e)
           if (nq + e < N) {
-            if constexpr (OUT == kF32) reinterpret_cast<float*>(dst)[e] = reinterpret_cast<const float*>(src)[e];
-            else reinterpret_cast<uint16_t*>(dst)[e] = reinterpret_cast<const uint16_t*>(src)[e];
+            if constexpr (CB == 4) reinterpret_cast<float*>(dst)[e] = reinterpret_cast<const float*>(src)[e];
+            else if constexpr (CB == 2) reinterpret_cast<uint16_t*>(dst)[e] = reinterpret_cast<const uint16_t*>(src)[e];
+            else dst[e] = src[e];
           }
       }
     }
   }
 };
 
+// Fold one lane's amax bits and the wave's saturation count of the
+// re-quantised output into the global results: a wave-wide reduction, then one
+// device-scope atomic per wave, skipped when the wave's maximum does not exceed
+// `seen` (the global value read before the epilogue began: the global maximum
+// only grows after it is cleared, so an older value is a safe lower bound) or
+// its count is 0.
+__device__ __forceinline__ void publish_requant_stats(uint32_t amax_bits_lane, uint32_t sat_wave, uint32_t seen,
+                                                      const RequantArgs& rq, int lane) {
+  const uint32_t m = wave_max_u32(amax_bits_lane);
+  if (lane == 0) {
+    if (rq.amax_bits && m > seen) atomicMax(rq.amax_bits, m);
+    if (rq.sat && sat_wave) atomicAdd(rq.sat, (unsigned long long)sat_wave);
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, int MODE>
 __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, int M, int N, int K,
     const float* __restrict__ sinv_a, const float* __restrict__ sinv_b, void* __restrict__ C,
-    int tiles_m, int tiles_n, int group_m) {
+    int tiles_m, int tiles_n, int group_m, RequantArgs rq) {
   constexpr int NW = WM * WN, NT = 64 * NW;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   // Output block of one matrix-core instruction: 16x16 (FP8 path), 32x32 (fp16 path).
@@ -270,12 +309,67 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
   uint8_t* const s1 = smem + STAGE;
   const int nfull = K / kBK;
 
+  // Four outputs c (already x sinv_a x sinv_b) of tile row r, columns n..n+3,
+  // into the staged pass (row r - r_lo).  The FP8 outputs are round_to_fp8 of
+  // fp32(c x out_scale), exactly as the cast kernels encode.  The amax of the
+  // unscaled c and the saturation count cover only outputs inside M x N;
+  // `mask` (a std::integral_constant) is false for tiles wholly inside C,
+  // which skips the bounds tests.  Saturation is |p| > max as a float
+  // comparison (false for NaN, true for Inf), counted by a wave ballot: FP8
+  // tiles go out in a single pass, so every lane is active at every call.
+  // Common case (no NaN among the four scaled values, tested through their
+  // sum, which an Inf - Inf also sends down the other path): the short
+  // encoder and a float maximum of |c|.  Otherwise the full rule and
+  // bit-pattern maxima (NaN above Inf).
+  float rq_maxf = 0.0f;
+  uint32_t rq_max = 0, rq_sat_wave = 0;
+  float rq_scale = 1.0f;
+  if constexpr (OUT == kOutE4M3 || OUT == kOutE5M2) rq_scale = rq.out_scale[0];
+  const int rows_left = (int)((M - m_base) < BM ? (M - m_base) : BM);
+  const int cols_left = (int)((N - n_base) < BN ? (N - n_base) : BN);
+  auto emit4 = [&](auto& tw, int r, int r_lo, int n, const v4f& c, auto mask) {
+    if constexpr (OUT == kF32 || OUT == kBF16) {
+      tw.put(r - r_lo, n, c);
+    } else {
+      constexpr int F = OUT == kOutE4M3 ? kE4M3 : kE5M2;
+      constexpr float kMax = Fp8Traits<F>::max_value;
+      const v4f p = c * rq_scale;
+      bool ok[4] = {true, true, true, true};
+      if constexpr (decltype(mask)::value) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ok[e] = r < rows_left && n + e < cols_left;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        rq_sat_wave += __builtin_popcountll(__builtin_amdgcn_ballot_w64(ok[e] && __builtin_fabsf(p[e]) > kMax));
+      const float t = (p[0] + p[1]) + (p[2] + p[3]);
+      uint32_t codes;
+      if (__builtin_expect(t == t, 1)) {
+        codes = encode4_finite<F>(p[0], p[1], p[2], p[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = ok[e] ? __builtin_fabsf(c[e]) : 0.0f;
+          rq_maxf = a > rq_maxf ? a : rq_maxf;
+        }
+      } else {
+        codes = encode4<F>(p[0], p[1], p[2], p[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t mb = ok[e] ? (f2u(c[e]) & 0x7FFFFFFFu) : 0u;
+          rq_max = mb > rq_max ? mb : rq_max;
+        }
+      }
+      tw.put_codes(r - r_lo, n, codes);
+    }
+  };
+
   // Stage the output tile through LDS in passes of as many rows as fit;
   // `emit(r_lo, r_hi, writer)` puts this lane's outputs of rows [r_lo, r_hi).
   auto write_tile = [&](auto&& emit) {
     using TW = TileWriter<OUT, BM, BN, NT>;
     constexpr int PASS = (2 * STAGE / TW::ROWB) < BM ? (2 * STAGE / TW::ROWB) : BM;
     static_assert(BM % PASS == 0, "output passes must tile the rows");
+    static_assert(PASS == BM || OUT == kF32 || OUT == kBF16, "FP8 tiles go out in one pass (ballot counts)");
     TW tw{smem, PASS};
 #pragma unroll 1
     for (int r0 = 0; r0 < BM; r0 += PASS) {
@@ -283,6 +377,19 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
       emit(r0, r0 + PASS, tw);
       __syncthreads();
       tw.flush(C, M, N, m_base + r0, n_base, t);
+    }
+  };
+  // `rows(r_lo, r_hi, writer, mask)`: write_tile with the bounds tests of the
+  // FP8 epilogue switched on only for tiles that cross the edge of C.
+  uint32_t rq_seen = 0;
+  auto write_tile_checked = [&](auto&& rows) {
+    auto with = [&](auto mask) { write_tile([&](int r_lo, int r_hi, auto& tw) { rows(r_lo, r_hi, tw, mask); }); };
+    if constexpr (OUT == kOutE4M3 || OUT == kOutE5M2) {
+      if (rq.amax_bits) rq_seen = __hip_atomic_load(rq.amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (rows_left == BM && cols_left == BN) with(std::false_type{});
+      else with(std::true_type{});
+    } else {
+      with(std::false_type{});
     }
   };
 
@@ -328,13 +435,13 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
     // Lane l holds row m = l & 15 of each 16x16 block (the A operand went
     // second) and columns n = 4(l >> 4) .. +3.
     const float sc = sinv_a[0] * sinv_b[0];
-    write_tile([&](int r_lo, int r_hi, auto& tw) {
+    write_tile_checked([&](int r_lo, int r_hi, auto& tw, auto mask) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int r = wm * WTM + i * 16 + (lane & 15);
         if (r < r_lo || r >= r_hi) continue;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) tw.put(r - r_lo, wn * WTN + j * 16 + 4 * (lane >> 4), acc[i][j] * sc);
+        for (int j = 0; j < FN; ++j) emit4(tw, r, r_lo, wn * WTN + j * 16 + 4 * (lane >> 4), acc[i][j] * sc, mask);
       }
     });
   } else {
@@ -379,7 +486,7 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
     // Lane l holds row m = l & 31 of each 32x32 block (the A operand went
     // second) and columns n = 8g + 4(l >> 5) + 0..3 in registers 4g..4g+3.
     const float sc = sinv_a[0] * sinv_b[0];
-    write_tile([&](int r_lo, int r_hi, auto& tw) {
+    write_tile_checked([&](int r_lo, int r_hi, auto& tw, auto mask) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int r = wm * WTM + i * 32 + (lane & 31);
@@ -389,10 +496,15 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const v4f v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-            tw.put(r - r_lo, wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5), v * sc);
+            emit4(tw, r, r_lo, wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5), v * sc, mask);
           }
       }
     });
+  }
+  if constexpr (OUT == kOutE4M3 || OUT == kOutE5M2) {
+    // |c| of the common path as bits (non-negative floats order as their bit patterns)
+    const uint32_t mf = f2u(rq_maxf);
+    publish_requant_stats(mf > rq_max ? mf : rq_max, rq_sat_wave, rq_seen, rq, lane);
   }
 }
 

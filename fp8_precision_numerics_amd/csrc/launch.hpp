@@ -25,6 +25,11 @@ hipError_t launch_gemm(const uint8_t* A, int fa, const uint8_t* B, int fb, int64
                        int64_t K, const float* sinv_a, const float* sinv_b, void* C, int ctype,
                        int accum, hipStream_t stream);
 
+hipError_t launch_gemm_requant(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t M, int64_t N,
+                               int64_t K, const float* sinv_a, const float* sinv_b, int out_fmt,
+                               const float* out_scale, uint8_t* Cq, float* amax, unsigned long long* sat,
+                               int accum, hipStream_t stream);
+
 hipError_t launch_grouped_gemm(const uint8_t* A, const float* sinv_a, const uint8_t* B,
                                const float* sinv_b, const int32_t* m_offsets, int G,
                                int64_t total_m, int64_t N, int64_t K, void* C, int ctype,

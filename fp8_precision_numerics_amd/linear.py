@@ -14,6 +14,9 @@ provides the device memory):
   Y = fp8_gemm(X_q, W_q).
 * backward: one cast pass of dY (E5M2) gives dY_q and dY_q^T;
   dX = fp8_gemm(dY_q, W_q^T), dW = fp8_gemm(dY_q^T, X_q^T).
+* forward_requant: the forward with Y re-quantised to FP8 in the GEMM's
+  epilogue with the scale of Y's own delayed-scaling state (§4.2.4: the
+  restore "combined with the next stage's scale"), recording Y's amax there.
 * update: each state pushes the amax its cast recorded and sets the scale
   for the next step.
 """
@@ -63,6 +66,20 @@ class Fp8Linear:
         self.state_w.quantize(w, q=self.qw, q_t=self.qw_t, stream=stream)
         _b.fp8_gemm(self.qx, "e4m3", self.qw, "e4m3", self.state_x.scale_inv, self.state_w.scale_inv, y,
                     accum=self.accum, stream=stream)
+
+    def forward_requant(self, x, w, yq, state_y: DelayedScalingState, stream=None):
+        """As forward, but Y leaves the GEMM as FP8 codes yq [tokens x out] in
+        state_y's format, cast with state_y's current scale; Y's amax and
+        saturation count go to state_y (state_y.update() then records them)."""
+        T, I, O = self.shape
+        self._check(x, T, I, "X")
+        self._check(w, O, I, "W")
+        self._check(yq, T, O, "Yq")
+        self.state_x.quantize(x, q=self.qx, q_t=self.qx_t, stream=stream)
+        self.state_w.quantize(w, q=self.qw, q_t=self.qw_t, stream=stream)
+        _b.fp8_gemm_requant(self.qx, "e4m3", self.qw, "e4m3", self.state_x.scale_inv, self.state_w.scale_inv,
+                            state_y.fmt, state_y.scale, yq, amax=state_y.amax, sat=state_y.sat,
+                            accum=self.accum, stream=stream)
 
     def backward(self, dy, dx, dw, stream=None):
         """Cast dY (E5M2, both orientations), then dx = dY W and dw = dY^T X from

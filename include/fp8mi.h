@@ -171,6 +171,37 @@ FP8MI_API int fp8_gemm(const uint8_t* A, int fa, const uint8_t* B, int fb, int64
              const float* sinv_a, const float* sinv_b, void* C, int ctype, int accum, void* stream);
 
 /*
+ * fp8_gemm_requant — fp8_gemm whose epilogue re-quantises the result to FP8
+ * with the next consumer's scale ([TE] §4.2.4: the x(1/scale) restore
+ * "combined with the next stage's scale"; each FP8 tensor's amax feeds its own
+ * delayed-scaling history), so the result never makes an fp32 / bf16 round
+ * trip through memory.
+ *
+ *   c[m][n]  = the fp32 value fp8_gemm stores for ctype = FP8MI_F32 (same
+ *              accumulation, same x sinv_a[0] x sinv_b[0])
+ *   Cq[m][n] = round_to_fp8(fp32(c[m][n] * out_scale[0]))  in out_fmt, exactly
+ *              as fp8_quantize encodes (RNE, saturating, NaN -> sign|0x7F)
+ *   amax     = max |c| over the M x N results, as the largest (bits & 0x7FFFFFFF)
+ *   sat      = #{ (m, n) : |fp32(c * out_scale)| > MAX }  (Inf counts, NaN does not)
+ * so the outputs equal fp8_gemm (fp32) followed by fp8_quantize of that result.
+ *
+ * A, B, fa, fb, sinv_a, sinv_b, M, N, K, accum  as for fp8_gemm.
+ * out_fmt    fp8mi_format of Cq (E4M3 for a forward activation, E5M2 for a gradient).
+ * out_scale  device, 1 fp32: normally the delayed scale of the output tensor's
+ *            own state (fp8_amax_update).
+ * Cq         device, [M x N] uint8 codes, 16-B aligned.
+ * amax       device, 1 fp32, overwritten, or NULL.  Feed it to the output
+ *            tensor's fp8_amax_update.
+ * sat        device, 1 uint64, overwritten, or NULL.
+ * M or N == 0 writes no codes (amax = 0, sat = 0).  A call clears amax and sat
+ * with a small kernel before the GEMM, so two calls in flight at once must not
+ * share them.
+ */
+FP8MI_API int fp8_gemm_requant(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t M, int64_t N, int64_t K,
+                     const float* sinv_a, const float* sinv_b, int out_fmt, const float* out_scale,
+                     uint8_t* Cq, float* amax, unsigned long long* sat, int accum, void* stream);
+
+/*
  * fp8_quantize_blockwise — current (not delayed) per-block scaling
  * ([FMT] "Deep dive": per-tensor or per-block scale factors; [DG]).
  *

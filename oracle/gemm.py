@@ -28,11 +28,22 @@ Definitions used here
 ``bf16_bracket``   for bf16 outputs: round-to-nearest-even is monotone, so a
                    bf16 result is acceptable iff it lies between the bf16
                    roundings of C64 - bound and C64 + bound.
+``requant_bracket`` for FP8 outputs re-quantised with the next consumer's
+                   scale s ("4.2 Hopper I", §4.2.4: the restore combined with
+                   the next stage's scale): the code is round_to_fp8(fp32(c*s))
+                   for the fp32 result c, which is only fixed up to the bound;
+                   fp32 rounding, the multiply by s > 0 and the encoding are
+                   all monotone, so an output code is acceptable iff its value
+                   lies between those of the encodings of C64 - bound and
+                   C64 + bound.  The same monotone argument brackets the amax
+                   of the results and the saturation count.
 ``grouped_gemm``   per expert g and per 128-wide K block kb,
                    C[m,n] += sinv_a[m,kb] * sinv_b[g, n//128, kb] *
                              sum_{k in kb} dec(a[m,k]) dec(b_g[n,k]).
 
-Parity status: the sum is pinned (exact integer dot products on small
+Parity status: requant_bracket is pinned by hand-computed codes (exact
+values, a round-to-even midpoint, saturation) in tests/test_oracle_gemm.py.
+The sum is pinned (exact integer dot products on small
 matrices and on sampled elements; one-hot, permutation, all-zero and
 all-max operands with closed-form results).  The fp32 accumulation ORDER of
 the device is not pinned; the device is held to the stated bound instead.
@@ -42,10 +53,10 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import codec
+from . import codec, scaling
 
 __all__ = ["dequant_gemm", "exact_dot", "exact_gemm_small", "abs_bound", "bf16_round",
-           "bf16_bracket", "grouped_gemm", "grouped_abs_bound", "INT_SHIFT"]
+           "bf16_bracket", "requant_bracket", "grouped_gemm", "grouped_abs_bound", "INT_SHIFT"]
 
 # Every finite value of the format is an integer multiple of 2**-INT_SHIFT.
 INT_SHIFT = {"e4m3": 9, "e5m2": 16}
@@ -115,6 +126,29 @@ def bf16_round(x) -> np.ndarray:
 def bf16_bracket(c64, bound):
     """(lo, hi) fp32 arrays such that a bf16 output y is within the bound iff lo <= y <= hi."""
     return bf16_round(c64 - bound), bf16_round(c64 + bound)
+
+
+def requant_bracket(c64, bound, out_scale, fmt) -> dict:
+    """Acceptance bracket of a GEMM output re-quantised to FP8 with `out_scale`.
+
+    Returns fp64 arrays ``lo``, ``hi`` (an output code q is acceptable iff
+    lo <= dec(q) <= hi), and the brackets ``amax`` = (lo, hi) of the amax of the
+    unscaled results and ``sat`` = (lo, hi) of the saturation count.  The fp32
+    values nearest to C64 -+ bound stand in for the extreme fp32 results (at
+    most one fp32 ulp outside the bound, which only widens the bracket)."""
+    c64 = np.asarray(c64, dtype=np.float64)
+    bound = np.asarray(bound, dtype=np.float64)
+    f = codec._fmt(fmt)
+    lo32 = (c64 - bound).astype(np.float32)
+    hi32 = (c64 + bound).astype(np.float32)
+    q_lo, _, _ = scaling.quantize(lo32, out_scale, f)
+    q_hi, _, _ = scaling.quantize(hi32, out_scale, f)
+    mag_lo = np.maximum(np.abs(c64) - bound, 0.0)
+    mag_hi = np.abs(c64) + bound
+    sat_lo = scaling.saturation_count(scaling._scaled(mag_lo.astype(np.float32), out_scale), f)
+    sat_hi = scaling.saturation_count(scaling._scaled(mag_hi.astype(np.float32), out_scale), f)
+    return {"lo": codec.decode(q_lo, f), "hi": codec.decode(q_hi, f),
+            "amax": (float(mag_lo.max(initial=0.0)), float(mag_hi.max(initial=0.0))), "sat": (sat_lo, sat_hi)}
 
 
 def _blocks(K: int, kb: int = 128):

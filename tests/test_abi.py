@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert fm.version() == 300
+    assert fm.version() == 400
     for code in (OK, ENULL, ESHAPE, EALIGN, EFMT, EDTYPE, ELAUNCH, EDEV, EACCUM):
         assert fm.status_string(code) and fm.status_string(code) != "unknown status"
     assert fm.status_string(12345) == "unknown status"
@@ -64,6 +64,21 @@ def test_quantize_argument_errors(lib):
     assert q(None, 0, 0, 16, 0, A16, A16, None, None, None, None, 0, None) == OK         # empty, no reductions
     assert q(A16, 0, 4, 16, 0, A16, A16, None, A16, None, A8, 64, None) == EALIGN       # workspace alignment
     assert q(A16, 0, 4, 16, 0, A16, A16, None, A16, None, A16, 8, None) == EALIGN       # workspace < 16 B
+
+
+def test_gemm_requant_argument_errors(lib):
+    g = lib.fp8_gemm_requant
+    #      A    fa  B    fb  M   N   K   sa   sb  ofmt out_s Cq  amax sat accum stream
+    assert g(A16, 0, A16, 0, 16, 16, 16, A16, A16, 7, A16, A16, None, None, 0, None) == EFMT     # out format
+    assert g(A16, 2, A16, 0, 16, 16, 16, A16, A16, 0, A16, A16, None, None, 0, None) == EFMT
+    assert g(A16, 0, A16, 0, 16, 16, 16, A16, A16, 0, A16, A16, None, None, 5, None) == EACCUM
+    assert g(A16, 0, A16, 0, 16, 16, 24, A16, A16, 0, A16, A16, None, None, 0, None) == EALIGN   # 16 | K
+    assert g(A16, 0, A16, 0, -1, 16, 16, A16, A16, 0, A16, A16, None, None, 0, None) == ESHAPE
+    assert g(A16, 0, A16, 0, 16, 16, 1 << 24, A16, A16, 0, A16, A16, None, None, 0, None) == ESHAPE
+    assert g(A16, 0, A16, 0, 16, 16, 16, A16, A16, 0, None, A16, None, None, 0, None) == ENULL    # no out scale
+    assert g(A16, 0, A16, 0, 16, 16, 16, A16, A16, 0, A16, None, None, None, 0, None) == ENULL    # no output
+    assert g(A16, 0, A16, 0, 16, 16, 16, A16, A16, 0, A16, A8, None, None, 0, None) == EALIGN
+    assert g(None, 0, None, 0, 0, 16, 16, None, None, 0, None, None, None, None, 0, None) == OK  # empty, no stats
 
 
 def test_amax_update_argument_errors(lib):

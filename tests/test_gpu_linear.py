@@ -8,7 +8,7 @@ import torch
 
 import fp8_precision_numerics_amd as fm
 from gpu_helpers import announce, device, f32, mfma8_bound, to_device, u8
-from oracle import gemm, linear, scaling
+from oracle import codec, gemm, linear, scaling
 from synth import dgrad_hybrid, fc1_forward
 
 pytestmark = pytest.mark.gpu
@@ -67,6 +67,43 @@ def test_linear_step_matches_oracle(T, I, O, accum):
         _check(f32(y), r["y"], bounds["y"])
         _check(f32(dx), r["dx"], bounds["dx"])
         _check(f32(dw), r["dw"], bounds["dw"])
+
+
+@pytest.mark.parametrize("accum", ["exact", "mfma_fp8"])
+def test_forward_requant_within_bracket(accum):
+    """The forward with Y re-quantised to E4M3 in the epilogue, with Y's own
+    delayed-scaling state over three steps: codes and the recorded amax within
+    the oracle's bracket of the step's exact product; Y's scale leaves 1 once
+    its first amax is recorded."""
+    dev = device()
+    T, I, O = 208, 272, 144
+    rng = np.random.default_rng(77)
+    layer = fm.Fp8Linear(T, I, O, accum=accum, device=dev)
+    st_y = fm.DelayedScalingState("e4m3", 16, device=dev)
+    refs = (scaling.DelayedScaling("e4m3"), scaling.DelayedScaling("e4m3"), scaling.DelayedScaling("e5m2"))
+    yq = torch.empty((T, O), dtype=torch.uint8, device=dev)
+    dy = np.zeros((T, O), dtype=np.float32)
+    for step in range(3):
+        x = (rng.standard_normal((T, I)) * (1 + step)).astype(np.float32)
+        w = (rng.standard_normal((O, I)) * 0.02).astype(np.float32)
+        announce(f"forward requant step {step} {accum}")
+        s_y = st_y.scale.item()
+        layer.forward_requant(to_device((x, "f32"), dev), to_device((w, "f32"), dev), yq, st_y)
+        torch.cuda.synchronize()
+        amax_y = st_y.amax.item()
+        layer.state_x.update()
+        layer.state_w.update()
+        st_y.update()
+        r = linear.hybrid_linear_step(x, w, dy, *refs)
+        assert np.array_equal(u8(layer.qx), r["qx"]) and np.array_equal(u8(layer.qw), r["qw"])
+        six, siw, _ = r["scale_inv"]
+        bound = r["bounds"]["y"] if accum == "exact" else mfma8_bound(r["qx"], "e4m3", r["qw"], "e4m3", six, siw)
+        br = gemm.requant_bracket(r["y"], bound, np.float32(s_y), "e4m3")
+        got = codec.decode(u8(yq), "e4m3")
+        assert np.all((got >= br["lo"]) & (got <= br["hi"]))
+        assert br["amax"][0] <= amax_y <= br["amax"][1]
+    # step 0 cast Y with scale 1; later steps with 448 / (max amax so far)
+    assert st_y.scale.item() != 1.0
 
 
 def test_linear_rejects_wrong_shapes():

@@ -154,3 +154,24 @@ def test_moe_counts_recipe():
     c = moe_token_counts()
     assert c.sum() == 16384 and c.size == 8
     assert np.all(c % 128 == 0) and c.min() >= 128 and c.max() <= 4096
+
+
+def test_requant_bracket_hand_values():
+    """Codes of re-quantised outputs, derived by hand from the formats."""
+    # zero bound: one code each; 3*2 = 6 and -0.5*2 = -1 exact, 1000*2 saturates to 448
+    r = gemm.requant_bracket(np.array([3.0, -0.5, 1000.0, 0.0]), np.zeros(4), np.float32(2.0), "e4m3")
+    assert list(r["lo"]) == [6.0, -1.0, 448.0, 0.0] and list(r["hi"]) == [6.0, -1.0, 448.0, 0.0]
+    assert r["amax"] == (1000.0, 1000.0) and r["sat"] == (1, 1)
+    # 1.0625 is the midpoint of E4M3 1.0 and 1.125: ties to even give 1.0; any positive bound admits 1.125
+    r = gemm.requant_bracket(np.array([1.0625]), np.array([0.0]), np.float32(1.0), "e4m3")
+    assert r["lo"][0] == 1.0 and r["hi"][0] == 1.0
+    r = gemm.requant_bracket(np.array([1.0625]), np.array([1e-6]), np.float32(1.0), "e4m3")
+    assert r["lo"][0] == 1.0 and r["hi"][0] == 1.125
+    # E5M2 around its max: c in [53248, 69632]; 53248 is the midpoint of 49152 (mantissa 10b) and
+    # 57344 (11b), so it rounds to the even 49152; 69632 saturates to 57344
+    r = gemm.requant_bracket(np.array([61440.0]), np.array([8192.0]), np.float32(1.0), "e5m2")
+    assert r["lo"][0] == 49152.0 and r["hi"][0] == 57344.0
+    assert r["sat"] == (0, 1) and r["amax"] == (53248.0, 69632.0)
+    # a bracket across zero: the amax bracket starts at 0, negative and positive codes both admitted
+    r = gemm.requant_bracket(np.array([0.25]), np.array([0.5]), np.float32(1.0), "e4m3")
+    assert r["lo"][0] == -0.25 and r["hi"][0] == 0.75 and r["amax"] == (0.0, 0.75)
