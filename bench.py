@@ -15,7 +15,8 @@ of the whole step); `roofline` is the GEMM kernel alone (HIP events around
 each launch on its stream); `extra` holds the delayed-scaling stream
 (32 x 8192x4096, HBM GB/s of the fused amax+cast), one HYBRID linear-layer
 training step at the FC1 shape (forward, dgrad, wgrad, each launch timed), the
-fine-grained MoE grouped GEMM and the vendor library's GEMMs on the FC1 shape; `cpu_baseline` times the CPU oracle on a
+fine-grained MoE grouped GEMM, one GPU's parts of an E5M2 gradient all-reduce
+and the vendor library's GEMMs on the FC1 shape; `cpu_baseline` times the CPU oracle on a
 bounded slice of the same step.
 """
 
@@ -350,6 +351,54 @@ def linear_bench(torch, fm, iters=10):
     return res
 
 
+def allreduce_bench(torch, fm, iters=20, ranks=8):
+    """One GPU's parts of an FP8 (E5M2) all-reduce of the FC1 weight gradient
+    (4096 x 16384 fp32) over `ranks` ranks: its amax pass, the shared scale, the
+    cast with that scale, and the fp32 sum of the `ranks` payloads of one
+    reduce-scattered chunk (67.1M / ranks codes each)."""
+    dev = torch.device("cuda:0")
+    n = 4096 * 16384
+    chunk = n // ranks
+    g = torch.empty(n, dtype=torch.float32, device=dev).normal_(0.0, 1e-4, generator=torch.Generator(dev).manual_seed(7))
+    amaxes = torch.zeros(ranks, dtype=torch.float32, device=dev)
+    scale = torch.empty(1, dtype=torch.float32, device=dev)
+    scale_inv = torch.empty(1, dtype=torch.float32, device=dev)
+    q = torch.empty(n, dtype=torch.uint8, device=dev)
+    out = torch.empty(chunk, dtype=torch.float32, device=dev)
+    ws = torch.empty(fm.QUANTIZE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    # the received chunk: `ranks` payloads, here the codes of this rank's own gradient chunks
+    recv = q.view(ranks, chunk)
+    t = {k: EventTimer(torch) for k in ("amax", "shared_scale", "cast", "dequant_sum")}
+    for i in range(iters + 3):
+        timed = i >= 3
+        with (t["amax"] if timed else _Null()):
+            fm.fp8_quantize(g, "e5m2", None, amax=amaxes[0:1], workspace=ws)
+        with (t["shared_scale"] if timed else _Null()):
+            fm.fp8_shared_scale(amaxes, "e5m2", scale, scale_inv)
+        with (t["cast"] if timed else _Null()):
+            fm.fp8_quantize(g, "e5m2", scale, q=q, workspace=ws)
+        with (t["dequant_sum"] if timed else _Null()):
+            fm.fp8_dequant_sum(recv, "e5m2", scale_inv, out)
+    torch.cuda.synchronize()
+    us = {k: statistics.mean(v.ms()) * 1e3 for k, v in t.items()}
+    gbs = {"amax": n * 4 / us["amax"] / 1e3, "cast": n * 5 / us["cast"] / 1e3,
+           "dequant_sum": (ranks * chunk + 4 * chunk) / us["dequant_sum"] / 1e3}
+    log(f"fp8 all-reduce parts (E5M2, {ranks} ranks, 67.1M-value gradient): amax {us['amax']:.1f} us "
+        f"({gbs['amax']:.0f} GB/s), shared scale {us['shared_scale']:.1f} us, cast {us['cast']:.1f} us "
+        f"({gbs['cast']:.0f} GB/s), sum of {ranks} payloads {us['dequant_sum']:.1f} us ({gbs['dequant_sum']:.0f} GB/s)")
+    del g, q, out, recv
+    torch.cuda.empty_cache()
+    return {"ranks": ranks, "values": n, "us": us, "gbs": gbs}
+
+
+class _Null:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        return False
+
+
 def moe_bench(torch, fm, iters=20):
     from synth import moe_grouped
 
@@ -507,6 +556,7 @@ def main():
         extra["stream"] = stream_bench(torch, fm, args.stream_dtype)
         extra["linear_step"] = linear_bench(torch, fm)
         extra["moe_grouped"] = moe_bench(torch, fm)
+        extra["grad_allreduce_parts"] = allreduce_bench(torch, fm)
         extra["vendor_reference"] = vendor_reference(torch)
     cpu = None
     if not args.quick and not args.no_cpu_baseline:

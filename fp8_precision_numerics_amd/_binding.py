@@ -17,7 +17,8 @@ import torch
 
 __all__ = ["E4M3", "E5M2", "F32", "BF16", "ACCUM_EXACT", "ACCUM_MFMA_FP8", "QUANTIZE_WORKSPACE_BYTES", "Fp8Error", "load_library", "library_path",
            "status_string", "version", "fp8_quantize", "fp8_amax_update", "fp8_gemm",
-           "fp8_quantize_blockwise", "fp8_grouped_gemm", "fp8_gemm_requant", "EXPORTED_SYMBOLS"]
+           "fp8_quantize_blockwise", "fp8_grouped_gemm", "fp8_gemm_requant", "fp8_shared_scale", "fp8_dequant_sum",
+           "EXPORTED_SYMBOLS"]
 
 E4M3, E5M2 = 0, 1
 F32, BF16 = 0, 1
@@ -27,7 +28,8 @@ ACCUMS = {"exact": ACCUM_EXACT, "mfma_fp8": ACCUM_MFMA_FP8, ACCUM_EXACT: ACCUM_E
           ACCUM_MFMA_FP8: ACCUM_MFMA_FP8}
 
 EXPORTED_SYMBOLS = ("fp8mi_status_string", "fp8mi_version", "fp8_quantize", "fp8_amax_update",
-                    "fp8_gemm", "fp8_quantize_blockwise", "fp8_grouped_gemm", "fp8_gemm_requant")
+                    "fp8_gemm", "fp8_quantize_blockwise", "fp8_grouped_gemm", "fp8_gemm_requant",
+                    "fp8_shared_scale", "fp8_dequant_sum")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -79,6 +81,10 @@ def load_library():
     lib.fp8_gemm_requant.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64, i64, vp, vp, ctypes.c_int, vp,
                                      vp, vp, vp, ctypes.c_int, vp]
     lib.fp8_gemm_requant.restype = ctypes.c_int
+    lib.fp8_shared_scale.argtypes = [vp, i32, ctypes.c_int, vp, vp, vp]
+    lib.fp8_shared_scale.restype = ctypes.c_int
+    lib.fp8_dequant_sum.argtypes = [vp, i32, i64, i64, ctypes.c_int, vp, vp, ctypes.c_int, vp]
+    lib.fp8_dequant_sum.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -245,6 +251,37 @@ def fp8_gemm_requant(a, fa, b, fb, sinv_a, sinv_b, out_fmt, out_scale, cq, amax=
         _call("fp8_gemm_requant", lib.fp8_gemm_requant(_p(a), _fmt(fa), _p(b), _fmt(fb), M, N, K, _p(sinv_a),
                                                        _p(sinv_b), _fmt(out_fmt), _p(out_scale), _p(cq), _p(amax),
                                                        _p(sat), _accum(accum), _stream(stream)))
+
+
+def fp8_shared_scale(amaxes, fmt, scale, scale_inv, stream=None) -> None:
+    """scale = MAX / max(amaxes) (and its inverse), shared by the ranks of an FP8 all-reduce."""
+    lib = load_library()
+    dev = amaxes.device
+    _check(amaxes, "amaxes", torch.float32, None, dev)
+    _check(scale, "scale", torch.float32, 1, dev)
+    _check(scale_inv, "scale_inv", torch.float32, 1, dev)
+    with torch.cuda.device(dev):
+        _call("fp8_shared_scale", lib.fp8_shared_scale(_p(amaxes), amaxes.numel(), _fmt(fmt), _p(scale),
+                                                       _p(scale_inv), _stream(stream)))
+
+
+def fp8_dequant_sum(q, fmt, scale_inv, out, stream=None) -> None:
+    """out[i] = (sum over rows r of q, in row order, of dec(q[r, i])) * scale_inv, fp32 sums.
+
+    q: [R x n] uint8 payloads (rows may be a strided view with a 16-byte multiple row stride)."""
+    lib = load_library()
+    dev = q.device
+    if not q.is_cuda or q.dim() != 2 or q.dtype != torch.uint8 or q.stride(1) != 1:
+        raise ValueError("q must be a [R x n] uint8 GPU tensor with contiguous rows")
+    _check(scale_inv, "scale_inv", torch.float32, 1, dev)
+    _check(out, "out", (torch.float32, torch.bfloat16), None, dev)
+    R, n = q.shape
+    if out.numel() != n:
+        raise ValueError(f"out must have {n} elements")
+    otype = F32 if out.dtype == torch.float32 else BF16
+    with torch.cuda.device(dev):
+        _call("fp8_dequant_sum", lib.fp8_dequant_sum(_p(q), R, n, q.stride(0), _fmt(fmt), _p(scale_inv), _p(out),
+                                                     otype, _stream(stream)))
 
 
 def fp8_quantize_blockwise(x, block_rows, fmt, q, scale_inv, stream=None) -> None:

@@ -65,7 +65,7 @@ const char* fp8mi_status_string(int status) {
   }
 }
 
-int fp8mi_version(void) { return 400; }
+int fp8mi_version(void) { return 500; }
 
 int fp8_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, const float* scale,
                  uint8_t* q, uint8_t* q_t, float* amax, unsigned long long* sat, void* workspace,
@@ -137,6 +137,30 @@ int fp8_gemm_requant(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t
   if (dev != FP8MI_OK) return dev;
   return launched(fp8mi::launch_gemm_requant(A, fa, B, fb, M, N, K, sinv_a, sinv_b, out_fmt, out_scale, Cq,
                                              amax, sat, accum, (hipStream_t)stream));
+}
+
+int fp8_shared_scale(const float* amaxes, int32_t R, int fmt, float* scale, float* scale_inv, void* stream) {
+  if (!fmt_ok(fmt)) return FP8MI_ERR_FORMAT;
+  if (R < 1 || R > 65536) return FP8MI_ERR_SHAPE;
+  if (!amaxes || !scale || !scale_inv) return FP8MI_ERR_NULL;
+  const int dev = check_device();
+  if (dev != FP8MI_OK) return dev;
+  return launched(fp8mi::launch_shared_scale(amaxes, R, fmt, scale, scale_inv, (hipStream_t)stream));
+}
+
+int fp8_dequant_sum(const uint8_t* q, int32_t R, int64_t n, int64_t stride, int fmt, const float* scale_inv,
+                    void* out, int otype, void* stream) {
+  if (!fmt_ok(fmt)) return FP8MI_ERR_FORMAT;
+  if (!dtype_ok(otype)) return FP8MI_ERR_DTYPE;
+  if (R < 1 || R > 65536 || n < 0 || n > kMaxElems || stride < n) return FP8MI_ERR_SHAPE;
+  if (stride > kMaxElems || (int64_t)(R - 1) > kMaxElems / (stride > 0 ? stride : 1)) return FP8MI_ERR_SHAPE;
+  if ((stride & 15) != 0) return FP8MI_ERR_ALIGN;
+  if (n == 0) return FP8MI_OK;
+  if (!q || !scale_inv || !out) return FP8MI_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out)) return FP8MI_ERR_ALIGN;
+  const int dev = check_device();
+  if (dev != FP8MI_OK) return dev;
+  return launched(fp8mi::launch_dequant_sum(q, R, n, stride, fmt, scale_inv, out, otype, (hipStream_t)stream));
 }
 
 int fp8_quantize_blockwise(const void* x, int xtype, int64_t rows, int64_t cols, int32_t block_rows,

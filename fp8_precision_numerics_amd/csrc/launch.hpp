@@ -35,4 +35,10 @@ hipError_t launch_grouped_gemm(const uint8_t* A, const float* sinv_a, const uint
                                int64_t total_m, int64_t N, int64_t K, void* C, int ctype,
                                int accum, hipStream_t stream);
 
+hipError_t launch_shared_scale(const float* amaxes, int R, int fmt, float* scale, float* scale_inv,
+                               hipStream_t stream);
+
+hipError_t launch_dequant_sum(const uint8_t* q, int R, int64_t n, int64_t stride, int fmt, const float* scale_inv,
+                              void* out, int otype, hipStream_t stream);
+
 }  // namespace fp8mi

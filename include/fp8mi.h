@@ -12,6 +12,9 @@
  *         scale factors, high-precision partial sums).
  *   [DG]  "#fp8" tag page (discuss.pytorch.kr), DeepGEMM entry (MoE grouped
  *         GEMM, two-level "promotion" of FP8 partial sums).
+ *   [DG-talk] the same page, the discussion of FP8 LLM training ("automatic
+ *         scaling" of gradients during the all-reduce); [FMT] use cases (E5M2
+ *         for gradient communication).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -200,6 +203,41 @@ FP8MI_API int fp8_gemm(const uint8_t* A, int fa, const uint8_t* B, int fb, int64
 FP8MI_API int fp8_gemm_requant(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t M, int64_t N, int64_t K,
                      const float* sinv_a, const float* sinv_b, int out_fmt, const float* out_scale,
                      uint8_t* Cq, float* amax, unsigned long long* sat, int accum, void* stream);
+
+/*
+ * fp8_shared_scale — the scale every rank of an FP8 gradient all-reduce casts
+ * with ([FMT] use cases: E5M2 gradient communication; [DG-talk] "automatic
+ * scaling" keeps gradients inside FP8's range during the all-reduce; [TE]
+ * §4.2.4 scale = MAX / amax).
+ *
+ *   m = max over r < R of amaxes[r]   (bit patterns of |.|: NaN > Inf > finite)
+ *   if 0 < m < Inf and s = fp32(MAX / m) is finite: *scale = s, *scale_inv = fp32(1 / s)
+ *   else: *scale = *scale_inv = 1
+ *
+ * amaxes     device, R fp32: each rank's gradient amax after a MAX (or gather)
+ *            exchange; on one GPU, the amaxes of the tensors that share a scale.
+ * scale, scale_inv  device, 1 fp32 each, overwritten.
+ * R in [1, 65536].
+ */
+FP8MI_API int fp8_shared_scale(const float* amaxes, int32_t R, int fmt, float* scale, float* scale_inv, void* stream);
+
+/*
+ * fp8_dequant_sum — the receiving side of an FP8 gradient all-reduce: the R
+ * ranks' FP8 payloads of one chunk, summed in fp32 and restored.
+ *
+ *   out[i] = fp32( fp32( sum over r = 0, 1, ..., R-1 IN THAT ORDER of dec(q[r*stride + i]) ) * scale_inv[0] )
+ *
+ * (fp32 additions left to right; the first term is dec(q[i]) itself, so -0
+ * stays -0.)  bf16 outputs are that value rounded to nearest even.
+ *
+ * q          device, R payloads of n codes of format fmt, payload r at q + r*stride;
+ *            16-B aligned, stride a multiple of 16, stride >= n.
+ * scale_inv  device, 1 fp32: the shared inverse scale (fp8_shared_scale).
+ * out        device, n of otype (fp32 or bf16), 16-B aligned.
+ * R in [1, 65536]; n may be 0.
+ */
+FP8MI_API int fp8_dequant_sum(const uint8_t* q, int32_t R, int64_t n, int64_t stride, int fmt, const float* scale_inv,
+                    void* out, int otype, void* stream);
 
 /*
  * fp8_quantize_blockwise — current (not delayed) per-block scaling

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert fm.version() == 400
+    assert fm.version() == 500
     for code in (OK, ENULL, ESHAPE, EALIGN, EFMT, EDTYPE, ELAUNCH, EDEV, EACCUM):
         assert fm.status_string(code) and fm.status_string(code) != "unknown status"
     assert fm.status_string(12345) == "unknown status"
@@ -79,6 +79,25 @@ def test_gemm_requant_argument_errors(lib):
     assert g(A16, 0, A16, 0, 16, 16, 16, A16, A16, 0, A16, None, None, None, 0, None) == ENULL    # no output
     assert g(A16, 0, A16, 0, 16, 16, 16, A16, A16, 0, A16, A8, None, None, 0, None) == EALIGN
     assert g(None, 0, None, 0, 0, 16, 16, None, None, 0, None, None, None, None, 0, None) == OK  # empty, no stats
+
+
+def test_allreduce_parts_argument_errors(lib):
+    sc, ds = lib.fp8_shared_scale, lib.fp8_dequant_sum
+    assert sc(A16, 4, 3, A16, A16, None) == EFMT
+    assert sc(A16, 0, 1, A16, A16, None) == ESHAPE
+    assert sc(A16, 65537, 1, A16, A16, None) == ESHAPE
+    assert sc(None, 4, 1, A16, A16, None) == ENULL
+    assert sc(A16, 4, 1, A16, None, None) == ENULL
+    #        q    R  n    stride fmt sinv out otype stream
+    assert ds(A16, 2, 64, 64, 7, A16, A16, 0, None) == EFMT
+    assert ds(A16, 2, 64, 64, 1, A16, A16, 9, None) == EDTYPE
+    assert ds(A16, 0, 64, 64, 1, A16, A16, 0, None) == ESHAPE
+    assert ds(A16, 2, 64, 32, 1, A16, A16, 0, None) == ESHAPE       # stride < n
+    assert ds(A16, 2, 64, 72, 1, A16, A16, 0, None) == EALIGN       # stride not a multiple of 16
+    assert ds(A8, 2, 64, 64, 1, A16, A16, 0, None) == EALIGN
+    assert ds(A16, 2, 64, 64, 1, A16, A8, 0, None) == EALIGN
+    assert ds(A16, 2, 64, 64, 1, None, A16, 0, None) == ENULL
+    assert ds(None, 2, 0, 0, 1, None, None, 0, None) == OK          # empty
 
 
 def test_amax_update_argument_errors(lib):

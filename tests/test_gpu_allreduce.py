@@ -1,0 +1,119 @@
+"""GPU parity: one GPU's parts of the FP8 gradient all-reduce (shared scale,
+and the fp32 sum of R ranks' FP8 payloads) bit for bit against the oracle,
+and the whole exchange simulated with R ranks' gradients on one GPU."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_precision_numerics_amd as fm
+from gpu_helpers import announce, device, f32, u8
+from oracle import allreduce, codec, gemm
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits_equal_nan(a, b):
+    a, b = np.asarray(a, dtype=np.float32), np.asarray(b, dtype=np.float32)
+    nan = np.isnan(a)
+    return np.array_equal(nan, np.isnan(b)) and np.array_equal(a[~nan].view(np.uint32), b[~nan].view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_decode_every_code(fmt):
+    dev = device()
+    q = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(1, 256).to(dev)
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    out = torch.empty(256, dtype=torch.float32, device=dev)
+    fm.fp8_dequant_sum(q, fmt, one, out)
+    torch.cuda.synchronize()
+    assert _bits_equal_nan(f32(out), codec.decode(np.arange(256, dtype=np.uint8), fmt).astype(np.float32))
+
+
+def _finite_codes(rng, shape, fmt):
+    f = codec.FORMATS[fmt]
+    return (rng.integers(0, f.max_code + 1, size=shape) | (rng.integers(0, 2, size=shape) << 7)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("R,n,pad", [(1, 1, 0), (2, 15, 16), (3, 17, 0), (8, 1000, 32), (9, 65541, 48),
+                                     (16, 4096, 0)])
+def test_dequant_sum_bit_exact(R, n, pad, fmt, out):
+    """Random finite codes over the whole range, payload rows padded to a
+    16-byte multiple (plus `pad`): fp32 sums in rank order, then x scale_inv."""
+    announce(f"dequant_sum R={R} n={n} {fmt} {out}")
+    dev = device()
+    rng = np.random.default_rng(R * 1000 + n)
+    stride = (n + 15) // 16 * 16 + pad
+    codes = _finite_codes(rng, (R, stride), fmt)
+    sinv = np.float32(3.7e-5)
+    buf = torch.from_numpy(codes).to(dev)
+    o = torch.empty(n, dtype=torch.float32 if out == "f32" else torch.bfloat16, device=dev)
+    fm.fp8_dequant_sum(buf[:, :n], fmt, torch.tensor([sinv], device=dev), o)
+    torch.cuda.synchronize()
+    want = allreduce.dequant_sum([codes[r, :n] for r in range(R)], fmt, sinv)
+    if out == "bf16":
+        want = gemm.bf16_round(want)
+    assert _bits_equal_nan(f32(o), want)
+
+
+@pytest.mark.parametrize("fmt", ["e5m2", "e4m3"])
+@pytest.mark.parametrize("R", [1, 4, 8])
+def test_simulated_allreduce_matches_oracle(R, fmt):
+    """R ranks' fp32 gradients (magnitudes spread over 10^4 between ranks) on
+    one GPU: each rank's amax (cast kernel, amax only), the shared scale, each
+    rank's cast with it, and the restored fp32 sum — all bit for bit."""
+    announce(f"simulated all-reduce R={R} {fmt}")
+    dev = device()
+    rng = np.random.default_rng(R + (7 if fmt == "e4m3" else 0))
+    n = 12345 * 16
+    grads = [(rng.standard_normal(n) * 10.0 ** rng.uniform(-6, -2)).astype(np.float32) for _ in range(R)]
+    g_dev = [torch.from_numpy(g).to(dev) for g in grads]
+    amaxes = torch.empty(R, dtype=torch.float32, device=dev)
+    for r in range(R):
+        fm.fp8_quantize(g_dev[r], fmt, None, amax=amaxes[r:r + 1])
+    scale = torch.empty(1, dtype=torch.float32, device=dev)
+    scale_inv = torch.empty(1, dtype=torch.float32, device=dev)
+    fm.fp8_shared_scale(amaxes, fmt, scale, scale_inv)
+    q = torch.empty((R, n), dtype=torch.uint8, device=dev)
+    for r in range(R):
+        fm.fp8_quantize(g_dev[r], fmt, scale, q=q[r])
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    fm.fp8_dequant_sum(q, fmt, scale_inv, out)
+    torch.cuda.synchronize()
+    ref = allreduce.fp8_allreduce(grads, fmt)
+    assert np.array_equal(f32(amaxes).view(np.uint32), np.float32(ref["amaxes"]).view(np.uint32))
+    assert f32(scale)[0] == ref["scale"] and f32(scale_inv)[0] == ref["scale_inv"]
+    assert np.array_equal(u8(q), np.stack(ref["payloads"]))
+    assert np.array_equal(f32(out).view(np.uint32), ref["sum"].view(np.uint32))
+
+
+def test_shared_scale_without_a_usable_amax_is_one():
+    dev = device()
+    for vals in ([0.0, 0.0], [1.0, float("nan")], [float("inf")]):
+        am = torch.tensor(vals, dtype=torch.float32, device=dev)
+        s = torch.full((1,), 5.0, device=dev)
+        si = torch.full((1,), 5.0, device=dev)
+        fm.fp8_shared_scale(am, "e5m2", s, si)
+        torch.cuda.synchronize()
+        assert s.item() == 1.0 and si.item() == 1.0
+
+
+@pytest.mark.timeout(300)
+def test_full_chunk_eight_ranks():
+    """The FC1 weight gradient (4096 x 16384 = 67.1M values) reduce-scattered
+    over 8 ranks: 8 E5M2 payloads of 8.39M codes summed into one fp32 chunk,
+    bit for bit."""
+    dev = device()
+    R, n = 8, 4096 * 16384 // 8
+    rng = np.random.default_rng(99)
+    codes = _finite_codes(rng, (R, n), "e5m2")
+    sinv = np.float32(1.0 / 12345.0)
+    announce("full chunk, 8 ranks")
+    buf = torch.from_numpy(codes).to(dev)
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    fm.fp8_dequant_sum(buf, "e5m2", torch.tensor([sinv], device=dev), out)
+    torch.cuda.synchronize()
+    want = allreduce.dequant_sum([codes[r] for r in range(R)], "e5m2", sinv)
+    assert np.array_equal(f32(out).view(np.uint32), want.view(np.uint32))
