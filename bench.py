@@ -15,8 +15,9 @@ of the whole step); `roofline` is the GEMM kernel alone (HIP events around
 each launch on its stream); `extra` holds the delayed-scaling stream
 (32 x 8192x4096, HBM GB/s of the fused amax+cast), one HYBRID linear-layer
 training step at the FC1 shape (forward, dgrad, wgrad, each launch timed), the
-fine-grained MoE grouped GEMM, one GPU's parts of an E5M2 gradient all-reduce
-and the vendor library's GEMMs on the FC1 shape; `cpu_baseline` times the CPU oracle on a
+fine-grained MoE grouped GEMM, one GPU's parts of an E5M2 gradient all-reduce,
+MXFP8 (block-32 quantisation and the block-scaled GEMM) on the FC1 shape, and
+the vendor library's GEMMs on that shape; `cpu_baseline` times the CPU oracle on a
 bounded slice of the same step.
 """
 
@@ -351,6 +352,46 @@ def linear_bench(torch, fm, iters=10):
     return res
 
 
+def mx_bench(torch, fm, iters=20):
+    """MXFP8 on the FC1 shape: the per-32-block quantisation of X (8192 x 4096)
+    and of W^T (16384 x 4096), both bf16 -> E4M3 codes + exponent bytes, and the
+    block-scaled GEMM X W^T -> bf16 on the FP8 matrix cores."""
+    from synth import fc1_forward
+
+    dev = torch.device("cuda:0")
+    M, K, N = 8192, 4096, 16384
+    d = fc1_forward(M, K, N, priors=False)
+    X = torch.from_numpy(d["X"].data.view("int16")).to(dev).view(torch.bfloat16)
+    Wt = torch.from_numpy(d["W"].data.view("int16")).to(dev).view(torch.bfloat16).t().contiguous()
+    del d
+    qx = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sx = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    qw = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    sw = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    t = {k: EventTimer(torch) for k in ("quantize_x", "quantize_w", "gemm")}
+    for i in range(iters + 3):
+        timed = i >= 3
+        with (t["quantize_x"] if timed else _Null()):
+            fm.fp8_quantize_mx(X, "e4m3", qx, sx)
+        with (t["quantize_w"] if timed else _Null()):
+            fm.fp8_quantize_mx(Wt, "e4m3", qw, sw)
+        with (t["gemm"] if timed else _Null()):
+            fm.fp8_gemm_mx(qx, "e4m3", sx, qw, "e4m3", sw, c)
+    torch.cuda.synchronize()
+    us = {k: statistics.mean(v.ms()) * 1e3 for k, v in t.items()}
+    flops = 2.0 * M * N * K
+    res = {"us": us, "gemm_tflops": flops / us["gemm"] / 1e6,
+           "gemm_frac_of_fp8_peak": flops / us["gemm"] / 1e6 / PEAK_FP8_TFLOPS,
+           "quantize_x_gbs": M * K * (2 + 1 + 1 / 32) / us["quantize_x"] / 1e3,
+           "quantize_w_gbs": N * K * (2 + 1 + 1 / 32) / us["quantize_w"] / 1e3}
+    log(f"mxfp8: quantize X {us['quantize_x']:.1f} us ({res['quantize_x_gbs']:.0f} GB/s), W {us['quantize_w']:.1f} us "
+        f"({res['quantize_w_gbs']:.0f} GB/s); gemm {us['gemm']:.1f} us ({res['gemm_tflops']:.0f} TFLOP/s)")
+    del X, Wt, qx, sx, qw, sw, c
+    torch.cuda.empty_cache()
+    return res
+
+
 def allreduce_bench(torch, fm, iters=20, ranks=8):
     """One GPU's parts of an FP8 (E5M2) all-reduce of the FC1 weight gradient
     (4096 x 16384 fp32) over `ranks` ranks: its amax pass, the shared scale, the
@@ -557,6 +598,7 @@ def main():
         extra["linear_step"] = linear_bench(torch, fm)
         extra["moe_grouped"] = moe_bench(torch, fm)
         extra["grad_allreduce_parts"] = allreduce_bench(torch, fm)
+        extra["mxfp8"] = mx_bench(torch, fm)
         extra["vendor_reference"] = vendor_reference(torch)
     cpu = None
     if not args.quick and not args.no_cpu_baseline:

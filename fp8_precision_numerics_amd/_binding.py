@@ -18,7 +18,7 @@ import torch
 __all__ = ["E4M3", "E5M2", "F32", "BF16", "ACCUM_EXACT", "ACCUM_MFMA_FP8", "QUANTIZE_WORKSPACE_BYTES", "Fp8Error", "load_library", "library_path",
            "status_string", "version", "fp8_quantize", "fp8_amax_update", "fp8_gemm",
            "fp8_quantize_blockwise", "fp8_grouped_gemm", "fp8_gemm_requant", "fp8_shared_scale", "fp8_dequant_sum",
-           "EXPORTED_SYMBOLS"]
+           "fp8_quantize_mx", "fp8_gemm_mx", "EXPORTED_SYMBOLS"]
 
 E4M3, E5M2 = 0, 1
 F32, BF16 = 0, 1
@@ -29,7 +29,7 @@ ACCUMS = {"exact": ACCUM_EXACT, "mfma_fp8": ACCUM_MFMA_FP8, ACCUM_EXACT: ACCUM_E
 
 EXPORTED_SYMBOLS = ("fp8mi_status_string", "fp8mi_version", "fp8_quantize", "fp8_amax_update",
                     "fp8_gemm", "fp8_quantize_blockwise", "fp8_grouped_gemm", "fp8_gemm_requant",
-                    "fp8_shared_scale", "fp8_dequant_sum")
+                    "fp8_shared_scale", "fp8_dequant_sum", "fp8_quantize_mx", "fp8_gemm_mx")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -85,6 +85,10 @@ def load_library():
     lib.fp8_shared_scale.restype = ctypes.c_int
     lib.fp8_dequant_sum.argtypes = [vp, i32, i64, i64, ctypes.c_int, vp, vp, ctypes.c_int, vp]
     lib.fp8_dequant_sum.restype = ctypes.c_int
+    lib.fp8_quantize_mx.argtypes = [vp, ctypes.c_int, i64, i64, ctypes.c_int, vp, vp, vp]
+    lib.fp8_quantize_mx.restype = ctypes.c_int
+    lib.fp8_gemm_mx.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, i64, i64, i64, vp, ctypes.c_int, vp]
+    lib.fp8_gemm_mx.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -282,6 +286,39 @@ def fp8_dequant_sum(q, fmt, scale_inv, out, stream=None) -> None:
     with torch.cuda.device(dev):
         _call("fp8_dequant_sum", lib.fp8_dequant_sum(_p(q), R, n, q.stride(0), _fmt(fmt), _p(scale_inv), _p(out),
                                                      otype, _stream(stream)))
+
+
+def fp8_quantize_mx(x, fmt, q, scales, stream=None) -> None:
+    """MXFP8: codes q [rows x cols] and one exponent code per 32 values of a row, scales [rows x cols/32]."""
+    lib = load_library()
+    dev = x.device
+    _check(x, "x", (torch.float32, torch.bfloat16), None, dev)
+    rows, cols = _rows_cols(x)
+    _check(q, "q", torch.uint8, rows * cols, dev)
+    _check(scales, "scales", torch.uint8, rows * (cols // 32), dev)
+    xtype = F32 if x.dtype == torch.float32 else BF16
+    with torch.cuda.device(dev):
+        _call("fp8_quantize_mx", lib.fp8_quantize_mx(_p(x), xtype, rows, cols, _fmt(fmt), _p(q), _p(scales),
+                                                     _stream(stream)))
+
+
+def fp8_gemm_mx(a, fa, sa, b, fb, sb, c, stream=None) -> None:
+    """C[M x N] = sum_k (dec(a) 2^(sa - 127)) (dec(b) 2^(sb - 127)) on MXFP8 operands a [M x K], b [N x K]."""
+    lib = load_library()
+    dev = a.device
+    _check(a, "a", torch.uint8, None, dev)
+    _check(b, "b", torch.uint8, None, dev)
+    M, K = a.shape
+    N, K2 = b.shape
+    _check(sa, "sa", torch.uint8, M * (K // 32), dev)
+    _check(sb, "sb", torch.uint8, N * (K // 32), dev)
+    _check(c, "c", (torch.float32, torch.bfloat16), None, dev)
+    if K2 != K or tuple(c.shape) != (M, N):
+        raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)}, c {tuple(c.shape)}")
+    ctype = F32 if c.dtype == torch.float32 else BF16
+    with torch.cuda.device(dev):
+        _call("fp8_gemm_mx", lib.fp8_gemm_mx(_p(a), _fmt(fa), _p(sa), _p(b), _fmt(fb), _p(sb), M, N, K, _p(c), ctype,
+                                             _stream(stream)))
 
 
 def fp8_quantize_blockwise(x, block_rows, fmt, q, scale_inv, stream=None) -> None:

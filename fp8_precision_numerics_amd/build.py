@@ -30,7 +30,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIBPATH = os.path.join(LIBDIR, "libfp8mi.so")
 BUILDDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.hip", "quantize.hip", "amax_update.hip", "gemm.hip", "gemm_requant.hip", "grouped_gemm.hip", "allreduce.hip"]
+SOURCES = ["api.hip", "quantize.hip", "amax_update.hip", "gemm.hip", "gemm_requant.hip", "grouped_gemm.hip", "allreduce.hip", "mx.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",
          "-mcode-object-version=5",

@@ -65,7 +65,7 @@ const char* fp8mi_status_string(int status) {
   }
 }
 
-int fp8mi_version(void) { return 500; }
+int fp8mi_version(void) { return 600; }
 
 int fp8_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, const float* scale,
                  uint8_t* q, uint8_t* q_t, float* amax, unsigned long long* sat, void* workspace,
@@ -161,6 +161,37 @@ int fp8_dequant_sum(const uint8_t* q, int32_t R, int64_t n, int64_t stride, int 
   const int dev = check_device();
   if (dev != FP8MI_OK) return dev;
   return launched(fp8mi::launch_dequant_sum(q, R, n, stride, fmt, scale_inv, out, otype, (hipStream_t)stream));
+}
+
+int fp8_quantize_mx(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, uint8_t* q, uint8_t* scales,
+                    void* stream) {
+  if (!dtype_ok(xtype)) return FP8MI_ERR_DTYPE;
+  if (!fmt_ok(fmt)) return FP8MI_ERR_FORMAT;
+  if (!dims_ok(rows, cols)) return FP8MI_ERR_SHAPE;
+  if ((cols & 31) != 0) return FP8MI_ERR_ALIGN;
+  if (rows * cols == 0) return FP8MI_OK;
+  if (!x || !q || !scales) return FP8MI_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q)) return FP8MI_ERR_ALIGN;
+  const int dev = check_device();
+  if (dev != FP8MI_OK) return dev;
+  return launched(fp8mi::launch_quantize_mx(x, xtype, rows, cols, fmt, q, scales, (hipStream_t)stream));
+}
+
+int fp8_gemm_mx(const uint8_t* A, int fa, const uint8_t* sa, const uint8_t* B, int fb, const uint8_t* sb, int64_t M,
+                int64_t N, int64_t K, void* C, int ctype, void* stream) {
+  if (!fmt_ok(fa) || !fmt_ok(fb)) return FP8MI_ERR_FORMAT;
+  if (!dtype_ok(ctype)) return FP8MI_ERR_DTYPE;
+  if (M < 0 || N < 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxGemmK) return FP8MI_ERR_SHAPE;
+  if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N)) return FP8MI_ERR_SHAPE;
+  if ((K & 127) != 0) return FP8MI_ERR_ALIGN;
+  if (((M + 127) / 128) * ((N + 127) / 128) > kMaxDim) return FP8MI_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8MI_OK;
+  if (!A || !sa || !B || !sb || !C) return FP8MI_ERR_NULL;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C) || ((uintptr_t)sa & 3) || ((uintptr_t)sb & 3))
+    return FP8MI_ERR_ALIGN;
+  const int dev = check_device();
+  if (dev != FP8MI_OK) return dev;
+  return launched(fp8mi::launch_gemm_mx(A, fa, sa, B, fb, sb, M, N, K, C, ctype, (hipStream_t)stream));
 }
 
 int fp8_quantize_blockwise(const void* x, int xtype, int64_t rows, int64_t cols, int32_t block_rows,

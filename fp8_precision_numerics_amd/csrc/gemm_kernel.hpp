@@ -43,6 +43,13 @@ struct RequantArgs {
   unsigned long long* sat;
 };
 
+// E8M0 block-scale matrices of an MXFP8 GEMM (one byte per 32 K values of a
+// row of A and of B); unused by the other modes.
+struct MxScales {
+  const uint8_t* a;
+  const uint8_t* b;
+};
+
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
@@ -67,6 +74,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 __device__ __forceinline__ void dma_lds16(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff, int soff) {
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(lds)
+               : "memory");
+}
+
+__device__ __forceinline__ void dma_lds4(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff, int soff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(lds)
                : "memory");
 }
 
@@ -251,6 +263,15 @@ struct TileWriter {
   }
 };
 
+// Rows of one output pass through the LDS: the largest power of two that fits
+// `bytes` and divides a tile of BM rows.
+template <int BM>
+constexpr int pass_rows(int bytes, int row_bytes) {
+  int p = BM;
+  while (p > 1 && p * row_bytes > bytes) p >>= 1;
+  return p;
+}
+
 // Fold one lane's amax bits and the wave's saturation count of the
 // re-quantised output into the global results: a wave-wide reduction, then one
 // device-scope atomic per wave, skipped when the wave's maximum does not exceed
@@ -266,18 +287,48 @@ __device__ __forceinline__ void publish_requant_stats(uint32_t amax_bits_lane, u
   }
 }
 
+// Block scales of one MXFP8 step: the four E8M0 bytes (one per 32-deep K block
+// of the 128-deep step) of every tile row of A, then of B, 4 bytes per row in
+// the stage's scale area.  Wave w fetches rows w*64 .. +63 of that list with
+// one dword load to LDS (lane i: row w*64 + i); rows past the edge of A or B
+// fall outside the buffer resource and read as zero.
+template <int BM, int BN, int NW>
+struct MxScaleLoader {
+  static_assert(BM + BN == 64 * NW && BM % 64 == 0, "one scale row per lane");
+  __amdgpu_buffer_rsrc_t r;
+  int voff, w;
+  __device__ __forceinline__ MxScaleLoader(const MxScales& sx, int64_t m0, int64_t M, int64_t n0, int64_t N, int kb,
+                                           int w_, int lane)
+      : w(w_) {
+    if (w < BM / 64) {
+      r = operand_rsrc(sx.a + m0 * kb, M - m0, kb);
+      voff = (w * 64 + lane) * kb;
+    } else {
+      r = operand_rsrc(sx.b + n0 * kb, N - n0, kb);
+      voff = (w * 64 + lane - BM) * kb;
+    }
+  }
+  __device__ __forceinline__ void issue(uint8_t* scale_area, int kt) const {
+    dma_lds4(r, lds_addr(scale_area) + w * 256, voff, kt * 4);
+  }
+};
+
 template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, int MODE>
 __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, int M, int N, int K,
     const float* __restrict__ sinv_a, const float* __restrict__ sinv_b, void* __restrict__ C,
-    int tiles_m, int tiles_n, int group_m, RequantArgs rq) {
+    int tiles_m, int tiles_n, int group_m, RequantArgs rq, MxScales mxs) {
   constexpr int NW = WM * WN, NT = 64 * NW;
   constexpr int WTM = BM / WM, WTN = BN / WN;
-  // Output block of one matrix-core instruction: 16x16 (FP8 path), 32x32 (fp16 path).
-  constexpr int BLK = MODE == kAccumMfma8 ? 16 : 32;
+  // Output block of one matrix-core instruction: 16x16 (FP8 paths), 32x32 (fp16 path).
+  constexpr bool MX = MODE == kAccumMx;
+  constexpr int BLK = MODE == kAccumExact ? 32 : 16;
   constexpr int FM = WTM / BLK, FN = WTN / BLK;
   static_assert(FM >= 1 && FN >= 1 && WTM % BLK == 0 && WTN % BLK == 0, "wave tile shape");
-  constexpr int STAGE = (BM + BN) * kBK;
+  // A stage: the A slab, the B slab, and (MXFP8) their block scales.
+  constexpr int SLABS = (BM + BN) * kBK;
+  constexpr int STAGE = SLABS + (MX ? (BM + BN) * 4 : 0);
+  static_assert(STAGE % 1024 == 0, "stages keep the slabs' 1 KiB alignment");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
   int tm, tn;
@@ -290,7 +341,12 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
   const bool ragged_k = (K % kBK) != 0;
 
   const SlabLoader<BM, BN, NW> slabs(A, m_base, M, B, n_base, N, K, w, lane);
-  auto issue_direct = [&](uint8_t* dst, int kt, int g) { slabs.issue(dst, kt, g); };
+  auto issue_direct = [&](uint8_t* dst, int kt, int g) {
+    slabs.issue(dst, kt, g);
+    if constexpr (MX) {
+      if (g == 0) MxScaleLoader<BM, BN, NW>(mxs, m_base, M, n_base, N, K / 32, w, lane).issue(dst + SLABS, kt);
+    }
+  };
   auto stage_ragged = [&](int kt, int stage) { slabs.ragged(smem + stage * STAGE, kt, t); };
 
   // Fragment reads.  FP8 path (16x16x128): lane l takes row l & 15 of a
@@ -367,8 +423,7 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
   // `emit(r_lo, r_hi, writer)` puts this lane's outputs of rows [r_lo, r_hi).
   auto write_tile = [&](auto&& emit) {
     using TW = TileWriter<OUT, BM, BN, NT>;
-    constexpr int PASS = (2 * STAGE / TW::ROWB) < BM ? (2 * STAGE / TW::ROWB) : BM;
-    static_assert(BM % PASS == 0, "output passes must tile the rows");
+    constexpr int PASS = pass_rows<BM>(2 * STAGE, TW::ROWB);
     static_assert(PASS == BM || OUT == kF32 || OUT == kBF16, "FP8 tiles go out in one pass (ballot counts)");
     TW tw{smem, PASS};
 #pragma unroll 1
@@ -393,33 +448,56 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
     }
   };
 
-  if constexpr (MODE == kAccumMfma8) {
+  if constexpr (MODE == kAccumMfma8 || MODE == kAccumMx) {
     v4f acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    // The instruction reads lane group h's first 16 bytes as K 16h .. 16h+15 and
+    // its last 16 as K 64+16h .. (measured).  Unscaled, any consistent K order
+    // gives the same sum, and granules 2h, 2h+1 are used; with block scales the
+    // hardware's K blocks must be the operand's, so granules h and h + 4.
     auto frag = [&](const uint8_t* tile, int row0) {
-      const uint4 lo = granule(tile, row0, 2 * hh), hi = granule(tile, row0, 2 * hh + 1);
+      const uint4 lo = granule(tile, row0, MX ? hh : 2 * hh), hi = granule(tile, row0, MX ? hh + 4 : 2 * hh + 1);
       return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     };
     static_assert(FN >= kDmaGroups, "one load group per leading B block");
     // A fragments of the step stay in registers; B fragments stream one
     // 16-row block ahead (bf[(j+1)&1] is read while the MFMAs of block j run).
+    // MXFP8: each fragment comes with its lane's E8M0 byte (row l & 15, K block
+    // l >> 4 of the step), passed to the instruction as that operand's scale.
     v8i af[FM], bf[2];
+    int sca[FM], scb[2];
+    auto scale_of = [&](const uint8_t* st, int list_row) {
+      return (int)st[SLABS + (list_row + (lane & 15)) * 4 + (lane >> 4)];
+    };
     auto load_frags = [&](const uint8_t* st) {
       bf[0] = frag(st + BM * kBK, wn * WTN);
+      if constexpr (MX) scb[0] = scale_of(st, BM + wn * WTN);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = frag(st, wm * WTM + i * 16);
+      for (int i = 0; i < FM; ++i) {
+        af[i] = frag(st, wm * WTM + i * 16);
+        if constexpr (MX) sca[i] = scale_of(st, wm * WTM + i * 16);
+      }
     };
     // Contract the stage at `st` (A fragments and the first B fragment already in registers).
     auto compute = [&](const uint8_t* st, auto&& dma) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         if (j < kDmaGroups) dma(j);
-        if (j + 1 < FN) bf[(j + 1) & 1] = frag(st + BM * kBK, wn * WTN + (j + 1) * 16);
+        if (j + 1 < FN) {
+          bf[(j + 1) & 1] = frag(st + BM * kBK, wn * WTN + (j + 1) * 16);
+          if constexpr (MX) scb[(j + 1) & 1] = scale_of(st, BM + wn * WTN + (j + 1) * 16);
+        }
 #pragma unroll
-        for (int i = 0; i < FM; ++i) acc[i][j] = mfma_fp8<FB, FA>(bf[j & 1], af[i], acc[i][j]);
+        for (int i = 0; i < FM; ++i) {
+          if constexpr (MX)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j & 1], af[i], acc[i][j], FB, FA, 0,
+                                                                         scb[j & 1], 0, sca[i]);
+          else
+            acc[i][j] = mfma_fp8<FB, FA>(bf[j & 1], af[i], acc[i][j]);
+        }
       }
     };
     // Scheduling hint: per B block, its two LDS reads ahead of its MFMAs.
@@ -433,8 +511,9 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
     run_main_loop(s0, s1, nfull, nk, ragged_k, issue_direct, stage_ragged, load_frags, compute, interleave);
 
     // Lane l holds row m = l & 15 of each 16x16 block (the A operand went
-    // second) and columns n = 4(l >> 4) .. +3.
-    const float sc = sinv_a[0] * sinv_b[0];
+    // second) and columns n = 4(l >> 4) .. +3.  MXFP8 carries its scales in
+    // the instruction: no per-tensor factor.
+    const float sc = MX ? 1.0f : sinv_a[0] * sinv_b[0];
     write_tile_checked([&](int r_lo, int r_hi, auto& tw, auto mask) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {

@@ -18,7 +18,13 @@
 //   accuracy price.
 //
 // Operand lanes.  16x16x128 (FP8 path): lane l supplies row l % 16 of each
-// operand and the 32-byte K slice l / 16 of the 128-deep K step.  32x32x16
+// operand and 32 bytes of the 128-deep K step: the instruction takes the first
+// 16 bytes of lane group h = l / 16 as K 16h .. 16h+15 and the last 16 as
+// K 64+16h .. 64+16h+15 (measured on MI355X), and in its block-scaled form
+// (MXFP8) applies the E8M0 scale that lane group b supplies to K 32b .. 32b+31.
+// Unscaled, the kernels simply give lane group h the 32-byte slice h; scaled,
+// they give it the 16-byte pieces h and h + 4, so the hardware's K blocks are
+// the operand's.  32x32x16
 // (fp16 path): lane l supplies row l % 32 and the 64-byte half l / 32 of the
 // step, of which sub-step s (16 deep) takes bytes [8s, 8s+8).  Any assignment
 // of K values to (lane, register) slots works as long as both operands use the
@@ -42,7 +48,9 @@
 namespace fp8mi {
 
 constexpr int kBK = 128;  // K bytes per main-loop step
-enum : int { kAccumExact = 0, kAccumMfma8 = 1 };
+// kAccumMx: the FP8 instruction with a power-of-two (E8M0) scale per 32-deep K
+// block of each operand row (MXFP8), applied by the instruction itself.
+enum : int { kAccumExact = 0, kAccumMfma8 = 1, kAccumMx = 2 };
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));

@@ -63,15 +63,6 @@ __device__ __forceinline__ bool expert_tile(const int32_t* __restrict__ m_offset
   return false;
 }
 
-// Rows of one output pass through the LDS: the largest power of two that fits
-// `bytes` and divides the tile.
-template <int BM>
-constexpr int pass_rows(int bytes, int row_bytes) {
-  int p = BM;
-  while (p > 1 && p * row_bytes > bytes) p >>= 1;
-  return p;
-}
-
 // ---------------------------------------------------------------------------
 // FP8 matrix-core mode.
 // ---------------------------------------------------------------------------

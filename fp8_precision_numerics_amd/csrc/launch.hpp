@@ -41,4 +41,10 @@ hipError_t launch_shared_scale(const float* amaxes, int R, int fmt, float* scale
 hipError_t launch_dequant_sum(const uint8_t* q, int R, int64_t n, int64_t stride, int fmt, const float* scale_inv,
                               void* out, int otype, hipStream_t stream);
 
+hipError_t launch_quantize_mx(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, uint8_t* q,
+                              uint8_t* scales, hipStream_t stream);
+
+hipError_t launch_gemm_mx(const uint8_t* A, int fa, const uint8_t* sa, const uint8_t* B, int fb, const uint8_t* sb,
+                          int64_t M, int64_t N, int64_t K, void* C, int ctype, hipStream_t stream);
+
 }  // namespace fp8mi

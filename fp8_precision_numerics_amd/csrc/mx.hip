@@ -1,0 +1,141 @@
+// MXFP8: FP8 elements with one power-of-two scale per 32 consecutive values of
+// a row, and the GEMM on such operands.
+//
+// "FP8 and low-precision formats", "Deep dive": per-tensor or per-block scale
+// factors keep values in FP8's usable range; MXFP8 goes further with shared
+// micro-scaling blocks.  "4.2 Hopper I — Transformer Engine·FP8", §4.2.4: the
+// scale is set from the amax so the values fit the format (MAX / amax).  Here a
+// block's scale is 2^e with e the smallest integer such that amax <= MAX * 2^e
+// (stored as the 8-bit exponent code e + 127), and each element is
+// round_to_fp8(x * 2^-e) with the cast's rule.
+//
+// The quantiser gives four lanes to a block (8 values each: one 16-byte bf16
+// load or two fp32 loads per lane, a wave covers 16 consecutive blocks), takes
+// the block amax with two lane exchanges, and writes 8 codes per lane and one
+// scale byte per block.  The GEMM is the dense kernel's FP8 path with the
+// scaled matrix-core instruction: V_MFMA_SCALE_F32_16X16X128_F8F6F4 takes, per
+// lane, the E8M0 byte of the 32-deep K block that lane's fragment covers, for
+// each operand, and applies both powers of two to the products (measured on
+// MI355X: the first operand's scale follows its rows and K blocks, the
+// second's likewise).
+#include "gemm_dispatch.hpp"
+#include "launch.hpp"
+
+namespace fp8mi {
+namespace {
+
+// Smallest e with amax <= MAX * 2^e for a finite, non-zero amax given as bits
+// (MAX = 1.75 * 2^EMAX for both formats), clamped to [-127, 127].
+template <int FMT>
+__device__ __forceinline__ int mx_exponent(uint32_t bits) {
+  constexpr int kEmax = FMT == kE4M3 ? 8 : 15;
+  int E;                 // amax = m * 2^E with m in [1, 2)
+  bool above;            // m > 1.75
+  const uint32_t ef = bits >> 23, mant = bits & 0x7FFFFFu;
+  if (ef != 0) {
+    E = (int)ef - 127;
+    above = mant > 0x600000u;
+  } else {               // subnormal: mant * 2^-149, leading bit at position p
+    const int p = 31 - __builtin_clz(mant);
+    E = p - 149;
+    above = (mant << 2) > (7u << p);
+  }
+  int e = E - kEmax + (above ? 1 : 0);
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  return e;
+}
+
+// 2^-e as an fp32 value, e in [-127, 127] (2^-127 is the subnormal 0x00400000).
+__device__ __forceinline__ float pow2_neg(int e) {
+  return e <= 126 ? u2f((uint32_t)(127 - e) << 23) : u2f(0x00400000u);
+}
+
+template <int FMT, int XT>
+__global__ __launch_bounds__(256) void quantize_mx_kernel(const void* __restrict__ x, int64_t nblocks,
+                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ scales) {
+  const int64_t lanes = nblocks * 4;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  // every lane of a wave runs the same number of iterations (the lane exchanges need the whole quad)
+  const int64_t first = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (int64_t base = first - (threadIdx.x & 63); base < lanes; base += step) {
+    const int64_t i = base + (threadIdx.x & 63);  // this lane's 8 values: [8i, 8i + 8)
+    const bool live = i < lanes;
+    float v[8];
+    if (live) {
+      if constexpr (XT == kBF16) {
+        const uint4 w = reinterpret_cast<const uint4*>(x)[i];
+        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+        v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+      } else {
+        const float4 a = reinterpret_cast<const float4*>(x)[2 * i], b = reinterpret_cast<const float4*>(x)[2 * i + 1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = 0.0f;
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t b = f2u(v[k]) & 0x7FFFFFFFu;
+      m = b > m ? b : m;
+    }
+    // the block's four lanes are a quad (lane & ~3)
+    uint32_t o = (uint32_t)__shfl_xor((int)m, 1, 64);
+    m = o > m ? o : m;
+    o = (uint32_t)__shfl_xor((int)m, 2, 64);
+    m = o > m ? o : m;
+    if (!live) continue;
+    const bool finite = m < 0x7F800000u;
+    const int e = (finite && m != 0u) ? mx_exponent<FMT>(m) : 0;
+    const float s = pow2_neg(e);
+    uint32_t c0, c1;
+    if (finite) {
+      c0 = encode4_finite<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+      c1 = encode4_finite<FMT>(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
+    } else {
+      c0 = encode4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+      c1 = encode4<FMT>(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
+    }
+    reinterpret_cast<uint2*>(q)[i] = make_uint2(c0, c1);
+    if ((i & 3) == 0) scales[i >> 2] = (uint8_t)(e + 127);
+  }
+}
+
+template <int FMT, int XT>
+hipError_t run_quantize_mx(const void* x, int64_t nblocks, uint8_t* q, uint8_t* scales, hipStream_t st) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t lanes = nblocks * 4;
+  int64_t blocks = (lanes + 255) / 256;
+  const int64_t cap = (int64_t)cus * 8;
+  blocks = blocks < 1 ? 1 : (blocks > cap ? cap : blocks);
+  hipLaunchKernelGGL((quantize_mx_kernel<FMT, XT>), dim3((unsigned)blocks), dim3(256), 0, st, x, nblocks, q, scales);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_mx(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, uint8_t* q,
+                              uint8_t* scales, hipStream_t stream) {
+  const int64_t nblocks = rows * (cols / 32);
+  if (nblocks == 0) return hipSuccess;
+  if (fmt == kE4M3) {
+    if (xtype == kBF16) return run_quantize_mx<kE4M3, kBF16>(x, nblocks, q, scales, stream);
+    return run_quantize_mx<kE4M3, kF32>(x, nblocks, q, scales, stream);
+  }
+  if (xtype == kBF16) return run_quantize_mx<kE5M2, kBF16>(x, nblocks, q, scales, stream);
+  return run_quantize_mx<kE5M2, kF32>(x, nblocks, q, scales, stream);
+}
+
+hipError_t launch_gemm_mx(const uint8_t* A, int fa, const uint8_t* sa, const uint8_t* B, int fb, const uint8_t* sb,
+                          int64_t M, int64_t N, int64_t K, void* C, int ctype, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const RequantArgs none{nullptr, nullptr, nullptr};
+  const MxScales mxs{sa, sb};
+  if (ctype == kBF16)
+    return gemm_dispatch_fmt<kBF16, kAccumMx>(A, fa, B, fb, M, N, K, nullptr, nullptr, C, none, stream, mxs);
+  return gemm_dispatch_fmt<kF32, kAccumMx>(A, fa, B, fb, M, N, K, nullptr, nullptr, C, none, stream, mxs);
+}
+
+}  // namespace fp8mi

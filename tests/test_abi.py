@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert fm.version() == 500
+    assert fm.version() == 600
     for code in (OK, ENULL, ESHAPE, EALIGN, EFMT, EDTYPE, ELAUNCH, EDEV, EACCUM):
         assert fm.status_string(code) and fm.status_string(code) != "unknown status"
     assert fm.status_string(12345) == "unknown status"
@@ -98,6 +98,24 @@ def test_allreduce_parts_argument_errors(lib):
     assert ds(A16, 2, 64, 64, 1, A16, A8, 0, None) == EALIGN
     assert ds(A16, 2, 64, 64, 1, None, A16, 0, None) == ENULL
     assert ds(None, 2, 0, 0, 1, None, None, 0, None) == OK          # empty
+
+
+def test_mx_argument_errors(lib):
+    qm, gm = lib.fp8_quantize_mx, lib.fp8_gemm_mx
+    assert qm(A16, 7, 4, 64, 0, A16, A16, None) == EDTYPE
+    assert qm(A16, 0, 4, 64, 9, A16, A16, None) == EFMT
+    assert qm(A16, 0, 4, 48, 0, A16, A16, None) == EALIGN        # 32 | cols
+    assert qm(A16, 0, -1, 64, 0, A16, A16, None) == ESHAPE
+    assert qm(A16, 0, 4, 64, 0, A16, None, None) == ENULL
+    assert qm(A8, 0, 4, 64, 0, A16, A16, None) == EALIGN
+    assert qm(None, 0, 0, 64, 0, None, None, None) == OK           # empty
+    #        A    fa  sa   B    fb  sb   M   N   K    C   ct stream
+    assert gm(A16, 0, A16, A16, 3, A16, 16, 16, 128, A16, 0, None) == EFMT
+    assert gm(A16, 0, A16, A16, 0, A16, 16, 16, 128, A16, 4, None) == EDTYPE
+    assert gm(A16, 0, A16, A16, 0, A16, 16, 16, 96, A16, 0, None) == EALIGN   # 128 | K
+    assert gm(A16, 0, None, A16, 0, A16, 16, 16, 128, A16, 0, None) == ENULL
+    assert gm(A16, 0, ctypes.c_void_p(0x10002), A16, 0, A16, 16, 16, 128, A16, 0, None) == EALIGN
+    assert gm(A16, 0, A16, A16, 0, A16, 16, 16, 1 << 24, A16, 0, None) == ESHAPE
 
 
 def test_amax_update_argument_errors(lib):
