@@ -365,9 +365,9 @@ def mx_bench(torch, fm, iters=20):
     Wt = torch.from_numpy(d["W"].data.view("int16")).to(dev).view(torch.bfloat16).t().contiguous()
     del d
     qx = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    sx = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    sx = torch.empty((K // 32, fm.mx_scale_ld(M)), dtype=torch.uint8, device=dev)
     qw = torch.empty((N, K), dtype=torch.uint8, device=dev)
-    sw = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+    sw = torch.empty((K // 32, fm.mx_scale_ld(N)), dtype=torch.uint8, device=dev)
     c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     t = {k: EventTimer(torch) for k in ("quantize_x", "quantize_w", "gemm")}
     for i in range(iters + 3):

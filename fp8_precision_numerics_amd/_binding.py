@@ -18,7 +18,8 @@ import torch
 __all__ = ["E4M3", "E5M2", "F32", "BF16", "ACCUM_EXACT", "ACCUM_MFMA_FP8", "QUANTIZE_WORKSPACE_BYTES", "Fp8Error", "load_library", "library_path",
            "status_string", "version", "fp8_quantize", "fp8_amax_update", "fp8_gemm",
            "fp8_quantize_blockwise", "fp8_grouped_gemm", "fp8_gemm_requant", "fp8_shared_scale", "fp8_dequant_sum",
-           "fp8_quantize_mx", "fp8_gemm_mx", "EXPORTED_SYMBOLS"]
+           "fp8_quantize_mx", "fp8_gemm_mx", "mx_scale_ld", "mx_scale_pos",
+           "EXPORTED_SYMBOLS"]
 
 E4M3, E5M2 = 0, 1
 F32, BF16 = 0, 1
@@ -288,14 +289,25 @@ def fp8_dequant_sum(q, fmt, scale_inv, out, stream=None) -> None:
                                                      otype, _stream(stream)))
 
 
+def mx_scale_ld(rows: int) -> int:
+    """Leading dimension of MXFP8 scale matrices: rows rounded up to 64."""
+    return (rows + 63) // 64 * 64
+
+
+def mx_scale_pos(r):
+    """Position of row r inside a K block of an MXFP8 scale matrix (rows permuted within groups of 64)."""
+    return (r & ~63) | ((r & 15) << 2) | ((r >> 4) & 3)
+
+
 def fp8_quantize_mx(x, fmt, q, scales, stream=None) -> None:
-    """MXFP8: codes q [rows x cols] and one exponent code per 32 values of a row, scales [rows x cols/32]."""
+    """MXFP8: codes q [rows x cols] and one exponent code per 32 values of a row, stored K-block major:
+    scales [cols/32 x mx_scale_ld(rows)], block b of row r at scales[b, mx_scale_pos(r)]."""
     lib = load_library()
     dev = x.device
     _check(x, "x", (torch.float32, torch.bfloat16), None, dev)
     rows, cols = _rows_cols(x)
     _check(q, "q", torch.uint8, rows * cols, dev)
-    _check(scales, "scales", torch.uint8, rows * (cols // 32), dev)
+    _check(scales, "scales", torch.uint8, (cols // 32) * mx_scale_ld(rows), dev)
     xtype = F32 if x.dtype == torch.float32 else BF16
     with torch.cuda.device(dev):
         _call("fp8_quantize_mx", lib.fp8_quantize_mx(_p(x), xtype, rows, cols, _fmt(fmt), _p(q), _p(scales),
@@ -303,15 +315,16 @@ def fp8_quantize_mx(x, fmt, q, scales, stream=None) -> None:
 
 
 def fp8_gemm_mx(a, fa, sa, b, fb, sb, c, stream=None) -> None:
-    """C[M x N] = sum_k (dec(a) 2^(sa - 127)) (dec(b) 2^(sb - 127)) on MXFP8 operands a [M x K], b [N x K]."""
+    """C[M x N] = sum_k (dec(a) 2^(sa - 127)) (dec(b) 2^(sb - 127)) on MXFP8 operands a [M x K], b [N x K];
+    sa [K/32 x mx_scale_ld(M)], sb [K/32 x mx_scale_ld(N)] as fp8_quantize_mx writes them."""
     lib = load_library()
     dev = a.device
     _check(a, "a", torch.uint8, None, dev)
     _check(b, "b", torch.uint8, None, dev)
     M, K = a.shape
     N, K2 = b.shape
-    _check(sa, "sa", torch.uint8, M * (K // 32), dev)
-    _check(sb, "sb", torch.uint8, N * (K // 32), dev)
+    _check(sa, "sa", torch.uint8, (K // 32) * mx_scale_ld(M), dev)
+    _check(sb, "sb", torch.uint8, (K // 32) * mx_scale_ld(N), dev)
     _check(c, "c", (torch.float32, torch.bfloat16), None, dev)
     if K2 != K or tuple(c.shape) != (M, N):
         raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)}, c {tuple(c.shape)}")

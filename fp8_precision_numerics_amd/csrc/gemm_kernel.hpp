@@ -287,29 +287,47 @@ __device__ __forceinline__ void publish_requant_stats(uint32_t amax_bits_lane, u
   }
 }
 
-// Block scales of one MXFP8 step: the four E8M0 bytes (one per 32-deep K block
-// of the 128-deep step) of every tile row of A, then of B, 4 bytes per row in
-// the stage's scale area.  Wave w fetches rows w*64 .. +63 of that list with
-// one dword load to LDS (lane i: row w*64 + i); rows past the edge of A or B
-// fall outside the buffer resource and read as zero.
+// Block scales of one MXFP8 step.  The scale matrices are stored K-block
+// major, rows permuted within groups of 64: byte (row r, block b) at
+// b * ld + mx_scale_pos(r), ld = rows rounded up to 64 (mx_scale_ld).  One K
+// block's scales of a 64-row group are then contiguous, and the four rows
+// c, c+16, c+32, c+48 of a group sit in one dword: the four 16-row fragments of
+// a 64-row wave tile take their scales from one LDS dword (the instruction
+// picks the byte).  A step needs blocks 4kt .. 4kt+3 of the tile's BM rows of A and
+// BN rows of B: BM + BN dwords of 4 rows each, one per lane of the workgroup
+// (entry e = 64 w + lane: A entries first, entry e of A covers block
+// e / (BM/4) and positions 4 (e % (BM/4)) .. +3), fetched with one dword load
+// to LDS per wave.  In the stage's scale area the byte of A row r, block b
+// sits at b * BM + mx_scale_pos(r), that of B row r at 4 BM + b * BN +
+// mx_scale_pos(r) (tile starts are multiples of 64).  Rows past the edge only
+// feed outputs that are not stored; bytes past the matrix read as zero.
+__host__ __device__ constexpr int64_t mx_scale_ld(int64_t rows) { return (rows + 63) / 64 * 64; }
+__host__ __device__ constexpr int64_t mx_scale_pos(int64_t r) { return (r & ~int64_t(63)) | ((r & 15) << 2) | ((r >> 4) & 3); }
+
 template <int BM, int BN, int NW>
 struct MxScaleLoader {
-  static_assert(BM + BN == 64 * NW && BM % 64 == 0, "one scale row per lane");
+  static_assert(BM + BN == 64 * NW && BM % 64 == 0, "one dword of scales per lane");
   __amdgpu_buffer_rsrc_t r;
-  int voff, w;
-  __device__ __forceinline__ MxScaleLoader(const MxScales& sx, int64_t m0, int64_t M, int64_t n0, int64_t N, int kb,
+  int voff, w, step;
+  __device__ __forceinline__ MxScaleLoader(const MxScales& sx, int64_t m0, int64_t M, int64_t n0, int64_t N, int K,
                                            int w_, int lane)
       : w(w_) {
+    const int e = w * 64 + lane;
     if (w < BM / 64) {
-      r = operand_rsrc(sx.a + m0 * kb, M - m0, kb);
-      voff = (w * 64 + lane) * kb;
+      const int64_t ld = mx_scale_ld(M);
+      r = operand_rsrc(sx.a, K / 32, ld);
+      voff = (int)((e / (BM / 4)) * ld + m0 + 4 * (e % (BM / 4)));
+      step = (int)(4 * ld);
     } else {
-      r = operand_rsrc(sx.b + n0 * kb, N - n0, kb);
-      voff = (w * 64 + lane - BM) * kb;
+      const int64_t ld = mx_scale_ld(N);
+      const int f = e - BM;
+      r = operand_rsrc(sx.b, K / 32, ld);
+      voff = (int)((f / (BN / 4)) * ld + n0 + 4 * (f % (BN / 4)));
+      step = (int)(4 * ld);
     }
   }
   __device__ __forceinline__ void issue(uint8_t* scale_area, int kt) const {
-    dma_lds4(r, lds_addr(scale_area) + w * 256, voff, kt * 4);
+    dma_lds4(r, lds_addr(scale_area) + w * 256, voff, kt * step);
   }
 };
 
@@ -344,7 +362,7 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
   auto issue_direct = [&](uint8_t* dst, int kt, int g) {
     slabs.issue(dst, kt, g);
     if constexpr (MX) {
-      if (g == 0) MxScaleLoader<BM, BN, NW>(mxs, m_base, M, n_base, N, K / 32, w, lane).issue(dst + SLABS, kt);
+      if (g == 0) MxScaleLoader<BM, BN, NW>(mxs, m_base, M, n_base, N, K, w, lane).issue(dst + SLABS, kt);
     }
   };
   auto stage_ragged = [&](int kt, int stage) { slabs.ragged(smem + stage * STAGE, kt, t); };
@@ -467,18 +485,24 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
     // 16-row block ahead (bf[(j+1)&1] is read while the MFMAs of block j run).
     // MXFP8: each fragment comes with its lane's E8M0 byte (row l & 15, K block
     // l >> 4 of the step), passed to the instruction as that operand's scale.
+    static_assert(!MX || (WTM % 64 == 0 && WTN % 64 == 0 && FM == 4), "MX scales: 64-row groups per wave tile");
     v8i af[FM], bf[2];
-    int sca[FM], scb[2];
-    auto scale_of = [&](const uint8_t* st, int list_row) {
-      return (int)st[SLABS + (list_row + (lane & 15)) * 4 + (lane >> 4)];
+    int sca = 0, scb[FN / 4 > 0 ? FN / 4 : 1] = {};
+    // The dword holding the scales of rows g64 + c + 16 i (i = 0..3, c = lane & 15)
+    // of the lane's K block; fragment i selects byte i.
+    auto scales4 = [&](const uint8_t* st, int area, int rows_in_area, int g64) {
+      return *reinterpret_cast<const int*>(st + SLABS + area + (lane >> 4) * rows_in_area + g64 + 4 * (lane & 15));
     };
     auto load_frags = [&](const uint8_t* st) {
       bf[0] = frag(st + BM * kBK, wn * WTN);
-      if constexpr (MX) scb[0] = scale_of(st, BM + wn * WTN);
+      if constexpr (MX) {
+        sca = scales4(st, 0, BM, wm * WTM);
+#pragma unroll
+        for (int h = 0; h < FN / 4; ++h) scb[h] = scales4(st, 4 * BM, BN, wn * WTN + 64 * h);
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         af[i] = frag(st, wm * WTM + i * 16);
-        if constexpr (MX) sca[i] = scale_of(st, wm * WTM + i * 16);
       }
     };
     // Contract the stage at `st` (A fragments and the first B fragment already in registers).
@@ -488,13 +512,11 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
         if (j < kDmaGroups) dma(j);
         if (j + 1 < FN) {
           bf[(j + 1) & 1] = frag(st + BM * kBK, wn * WTN + (j + 1) * 16);
-          if constexpr (MX) scb[(j + 1) & 1] = scale_of(st, BM + wn * WTN + (j + 1) * 16);
         }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           if constexpr (MX)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j & 1], af[i], acc[i][j], FB, FA, 0,
-                                                                         scb[j & 1], 0, sca[i]);
+            acc[i][j] = mfma_fp8_scaled<FB, FA>(bf[j & 1], af[i], acc[i][j], j & 3, scb[j >> 2], i, sca);
           else
             acc[i][j] = mfma_fp8<FB, FA>(bf[j & 1], af[i], acc[i][j]);
         }

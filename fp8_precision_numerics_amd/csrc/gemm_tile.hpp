@@ -64,6 +64,34 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& first, const v8i& second, con
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, FA, FB, 0, 0, 0, 0);
 }
 
+// The block-scaled form: s1 / s2 hold E8M0 codes, byte sel1 / sel2 of each is
+// the scale of this lane's K block of the first / second operand.  The byte
+// selectors are instruction fields, so they must be compile-time constants:
+// in the kernels' unrolled loops every call resolves to one case.
+template <int F1, int F2>
+__device__ __forceinline__ v4f mfma_fp8_scaled(const v8i& first, const v8i& second, const v4f& c, int sel1, int s1,
+                                               int sel2, int s2) {
+  switch (sel1 * 4 + sel2) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, F1, F2, 0, s1, 0, s2);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, F1, F2, 0, s1, 1, s2);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, F1, F2, 0, s1, 2, s2);
+    case 3: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, F1, F2, 0, s1, 3, s2);
+    case 4: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, F1, F2, 1, s1, 0, s2);
+    case 5: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, F1, F2, 1, s1, 1, s2);
+    case 6: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, F1, F2, 1, s1, 2, s2);
+    case 7: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, F1, F2, 1, s1, 3, s2);
+    case 8: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, F1, F2, 2, s1, 0, s2);
+    case 9: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, F1, F2, 2, s1, 1, s2);
+    case 10: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, F1, F2, 2, s1, 2, s2);
+    case 11: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, F1, F2, 2, s1, 3, s2);
+    case 12: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, F1, F2, 3, s1, 0, s2);
+    case 13: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, F1, F2, 3, s1, 1, s2);
+    case 14: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, F1, F2, 3, s1, 2, s2);
+    case 15: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, F1, F2, 3, s1, 3, s2);
+    default: __builtin_unreachable();
+  }
+}
+
 // Eight FP8 codes (bytes of w0 then w1) widened exactly to fp16.
 template <int F>
 __device__ __forceinline__ v8h widen8(uint32_t w0, uint32_t w1) {

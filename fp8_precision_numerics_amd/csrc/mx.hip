@@ -12,7 +12,8 @@
 // The quantiser gives four lanes to a block (8 values each: one 16-byte bf16
 // load or two fp32 loads per lane, a wave covers 16 consecutive blocks), takes
 // the block amax with two lane exchanges, and writes 8 codes per lane and one
-// scale byte per block.  The GEMM is the dense kernel's FP8 path with the
+// scale byte per block, K-block major so that the GEMM's per-step scale loads
+// are contiguous.  The GEMM is the dense kernel's FP8 path with the
 // scaled matrix-core instruction: V_MFMA_SCALE_F32_16X16X128_F8F6F4 takes, per
 // lane, the E8M0 byte of the 32-deep K block that lane's fragment covers, for
 // each operand, and applies both powers of two to the products (measured on
@@ -50,9 +51,13 @@ __device__ __forceinline__ float pow2_neg(int e) {
   return e <= 126 ? u2f((uint32_t)(127 - e) << 23) : u2f(0x00400000u);
 }
 
+// Scale bytes go K-block major, rows permuted within groups of 64 (block b of
+// row r at b * ld + mx_scale_pos(r); ld = rows rounded up to 64), the layout
+// the GEMM reads (gemm_kernel.hpp, MxScaleLoader).
 template <int FMT, int XT>
-__global__ __launch_bounds__(256) void quantize_mx_kernel(const void* __restrict__ x, int64_t nblocks,
-                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ scales) {
+__global__ __launch_bounds__(256) void quantize_mx_kernel(const void* __restrict__ x, int64_t nblocks, int64_t nbr,
+                                                          int64_t ld, uint8_t* __restrict__ q,
+                                                          uint8_t* __restrict__ scales) {
   const int64_t lanes = nblocks * 4;
   const int64_t step = (int64_t)gridDim.x * blockDim.x;
   // every lane of a wave runs the same number of iterations (the lane exchanges need the whole quad)
@@ -98,19 +103,24 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const void* __restrict
       c1 = encode4<FMT>(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
     }
     reinterpret_cast<uint2*>(q)[i] = make_uint2(c0, c1);
-    if ((i & 3) == 0) scales[i >> 2] = (uint8_t)(e + 127);
+    if ((i & 3) == 0) {
+      const int64_t blk = i >> 2, r = blk / nbr;
+      scales[(blk - r * nbr) * ld + mx_scale_pos(r)] = (uint8_t)(e + 127);
+    }
   }
 }
 
 template <int FMT, int XT>
-hipError_t run_quantize_mx(const void* x, int64_t nblocks, uint8_t* q, uint8_t* scales, hipStream_t st) {
+hipError_t run_quantize_mx(const void* x, int64_t nblocks, int64_t nbr, int64_t ld, uint8_t* q, uint8_t* scales,
+                           hipStream_t st) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const int64_t lanes = nblocks * 4;
   int64_t blocks = (lanes + 255) / 256;
   const int64_t cap = (int64_t)cus * 8;
   blocks = blocks < 1 ? 1 : (blocks > cap ? cap : blocks);
-  hipLaunchKernelGGL((quantize_mx_kernel<FMT, XT>), dim3((unsigned)blocks), dim3(256), 0, st, x, nblocks, q, scales);
+  hipLaunchKernelGGL((quantize_mx_kernel<FMT, XT>), dim3((unsigned)blocks), dim3(256), 0, st, x, nblocks, nbr, ld, q,
+                     scales);
   return hipGetLastError();
 }
 
@@ -118,14 +128,14 @@ hipError_t run_quantize_mx(const void* x, int64_t nblocks, uint8_t* q, uint8_t* 
 
 hipError_t launch_quantize_mx(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, uint8_t* q,
                               uint8_t* scales, hipStream_t stream) {
-  const int64_t nblocks = rows * (cols / 32);
+  const int64_t nbr = cols / 32, nblocks = rows * nbr, ld = mx_scale_ld(rows);
   if (nblocks == 0) return hipSuccess;
   if (fmt == kE4M3) {
-    if (xtype == kBF16) return run_quantize_mx<kE4M3, kBF16>(x, nblocks, q, scales, stream);
-    return run_quantize_mx<kE4M3, kF32>(x, nblocks, q, scales, stream);
+    if (xtype == kBF16) return run_quantize_mx<kE4M3, kBF16>(x, nblocks, nbr, ld, q, scales, stream);
+    return run_quantize_mx<kE4M3, kF32>(x, nblocks, nbr, ld, q, scales, stream);
   }
-  if (xtype == kBF16) return run_quantize_mx<kE5M2, kBF16>(x, nblocks, q, scales, stream);
-  return run_quantize_mx<kE5M2, kF32>(x, nblocks, q, scales, stream);
+  if (xtype == kBF16) return run_quantize_mx<kE5M2, kBF16>(x, nblocks, nbr, ld, q, scales, stream);
+  return run_quantize_mx<kE5M2, kF32>(x, nblocks, nbr, ld, q, scales, stream);
 }
 
 hipError_t launch_gemm_mx(const uint8_t* A, int fa, const uint8_t* sa, const uint8_t* B, int fb, const uint8_t* sb,

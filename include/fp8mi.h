@@ -253,8 +253,16 @@ FP8MI_API int fp8_dequant_sum(const uint8_t* q, int32_t R, int64_t n, int64_t st
  *
  * x       device, [rows x cols] of xtype, 16-B aligned; cols a multiple of 32.
  * q       device, [rows x cols] uint8 codes, 16-B aligned.
- * scales  device, [rows x cols/32] uint8 exponent codes (row-major).
+ * scales  device, [cols/32 x FP8MI_MX_SCALE_LD(rows)] uint8 exponent codes,
+ *         K-block major with rows permuted inside groups of 64: the code of
+ *         block b of row r at scales[b * ld + FP8MI_MX_SCALE_POS(r)] (the
+ *         layout fp8_gemm_mx reads: one K block's codes of a 64-row group are
+ *         contiguous, rows c, c+16, c+32, c+48 of a group share a dword).
+ *         Positions of rows >= rows are not written.
  */
+#define FP8MI_MX_SCALE_LD(rows) ((((int64_t)(rows)) + 63) / 64 * 64)
+#define FP8MI_MX_SCALE_POS(r) \
+  ((((int64_t)(r)) & ~(int64_t)63) | ((((int64_t)(r)) & 15) << 2) | ((((int64_t)(r)) >> 4) & 3))
 FP8MI_API int fp8_quantize_mx(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, uint8_t* q,
                     uint8_t* scales, void* stream);
 
@@ -267,9 +275,10 @@ FP8MI_API int fp8_quantize_mx(const void* x, int xtype, int64_t rows, int64_t co
  * 32-deep block are equal powers of two, so they do not change that model.
  *
  * A, B    device, [M x K] and [N x K] uint8 codes (K contiguous), 16-B aligned.
- * sa, sb  device, [M x K/32] and [N x K/32] exponent codes as fp8_quantize_mx
- *         writes them, 4-B aligned.  Code 255 (NaN) is not produced by the
- *         quantiser; its effect here is the instruction's.
+ * sa, sb  device, [K/32 x FP8MI_MX_SCALE_LD(M)] and [K/32 x FP8MI_MX_SCALE_LD(N)]
+ *         exponent codes in fp8_quantize_mx's layout, 4-B aligned.  Code 255 (NaN) is not produced by the quantiser; its effect
+ *         here is the instruction's.  The pad bytes only feed outputs that are
+ *         not stored.
  * C       device, [M x N] fp32 or bf16, 16-B aligned.
  * K must be a multiple of 128, K <= 2^23.
  */

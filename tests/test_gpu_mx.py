@@ -41,11 +41,11 @@ def test_quantize_mx_bit_exact(shape, fmt, dtype):
     xw = scaling.widen(h.data, dtype)
     dev = device()
     q = torch.empty(shape, dtype=torch.uint8, device=dev)
-    s = torch.empty((shape[0], shape[1] // 32), dtype=torch.uint8, device=dev)
+    s = torch.empty((shape[1] // 32, fm.mx_scale_ld(shape[0])), dtype=torch.uint8, device=dev)
     fm.fp8_quantize_mx(to_device(h, dev), fmt, q, s)
     torch.cuda.synchronize()
     wq, ws = mx.quantize_mx(xw, fmt)
-    assert np.array_equal(u8(s), ws)
+    assert np.array_equal(u8(s)[:, fm.mx_scale_pos(np.arange(shape[0]))].T, ws)   # K-block major, rows permuted
     assert np.array_equal(u8(q), wq)
 
 
@@ -54,6 +54,16 @@ def _rand_mx(rng, rows, K, fmt, lo=112, hi=142):
     q = (rng.integers(0, f.max_code + 1, size=(rows, K)) | (rng.integers(0, 2, size=(rows, K)) << 7)).astype(np.uint8)
     s = rng.integers(lo, hi, size=(rows, K // 32)).astype(np.uint8)
     return q, s
+
+
+def _dev_scales(s, dev, pad=127):
+    """Row-major [rows x K/32] exponent codes -> the library's layout on the
+    device: [K/32 x mx_scale_ld(rows)], row r at position mx_scale_pos(r)
+    (pad bytes = `pad`)."""
+    rows, nb = s.shape
+    out = np.full((nb, fm.mx_scale_ld(rows)), pad, dtype=np.uint8)
+    out[:, fm.mx_scale_pos(np.arange(rows))] = s.T
+    return torch.from_numpy(out).to(dev)
 
 
 def _check_mx(c_gpu, qa, sa, fa, qb, sb, fb, out):
@@ -81,8 +91,8 @@ def test_gemm_mx_within_error_model(M, N, K, fa, fb, out):
     qb, sb = _rand_mx(rng, N, K, fb)
     dev = device()
     c = torch.empty((M, N), dtype=torch.float32 if out == "f32" else torch.bfloat16, device=dev)
-    fm.fp8_gemm_mx(torch.from_numpy(qa).to(dev), fa, torch.from_numpy(sa).to(dev), torch.from_numpy(qb).to(dev), fb,
-                   torch.from_numpy(sb).to(dev), c)
+    fm.fp8_gemm_mx(torch.from_numpy(qa).to(dev), fa, _dev_scales(sa, dev), torch.from_numpy(qb).to(dev), fb,
+                   _dev_scales(sb, dev, pad=255), c)
     torch.cuda.synchronize()
     _check_mx(f32(c), qa, sa, fa, qb, sb, fb, out)
 
@@ -99,8 +109,8 @@ def test_gemm_mx_block_scales_select_blocks():
     sa = np.tile(127 + np.arange(nb), (M, 1)).astype(np.uint8)
     sb = (127 - np.arange(nb)[None, :] + (np.arange(N) % 3)[:, None]).astype(np.uint8)
     c = torch.empty((M, N), dtype=torch.float32, device=dev)
-    fm.fp8_gemm_mx(torch.from_numpy(qa).to(dev), "e4m3", torch.from_numpy(sa).to(dev), torch.from_numpy(qb).to(dev),
-                   "e4m3", torch.from_numpy(sb).to(dev), c)
+    fm.fp8_gemm_mx(torch.from_numpy(qa).to(dev), "e4m3", _dev_scales(sa, dev), torch.from_numpy(qb).to(dev),
+                   "e4m3", _dev_scales(sb, dev), c)
     torch.cuda.synchronize()
     want = 32.0 * nb * 2.0 ** (np.arange(N) % 3)
     assert np.array_equal(f32(c), np.tile(want, (M, 1)).astype(np.float32))
@@ -117,9 +127,9 @@ def test_fc1_mx_full_size():
     X = d["X"]
     W = HostTensor(np.ascontiguousarray(d["W"].data.T), "bf16")     # 16384 x 4096: rows = output features
     qx = torch.empty((8192, 4096), dtype=torch.uint8, device=dev)
-    sx = torch.empty((8192, 128), dtype=torch.uint8, device=dev)
+    sx = torch.empty((128, 8192), dtype=torch.uint8, device=dev)
     qw = torch.empty((16384, 4096), dtype=torch.uint8, device=dev)
-    sw = torch.empty((16384, 128), dtype=torch.uint8, device=dev)
+    sw = torch.empty((128, 16384), dtype=torch.uint8, device=dev)
     announce("fc1 mx full size: quantize + gemm")
     fm.fp8_quantize_mx(to_device(X, dev), "e4m3", qx, sx)
     fm.fp8_quantize_mx(to_device(W, dev), "e4m3", qw, sw)
@@ -131,7 +141,8 @@ def test_fc1_mx_full_size():
     rows_w = np.concatenate([rng.choice(16384, 24, replace=False), [0, 16383]])
     wqx, wsx = mx.quantize_mx(scaling.widen(X.data[rows_x], "bf16"), "e4m3")
     wqw, wsw = mx.quantize_mx(scaling.widen(W.data[rows_w], "bf16"), "e4m3")
-    qx_h, sx_h, qw_h, sw_h = u8(qx)[rows_x], u8(sx)[rows_x], u8(qw)[rows_w], u8(sw)[rows_w]
+    qx_h, qw_h = u8(qx)[rows_x], u8(qw)[rows_w]
+    sx_h, sw_h = u8(sx)[:, fm.mx_scale_pos(rows_x)].T, u8(sw)[:, fm.mx_scale_pos(rows_w)].T
     assert np.array_equal(qx_h, wqx) and np.array_equal(sx_h, wsx)
     assert np.array_equal(qw_h, wqw) and np.array_equal(sw_h, wsw)
     got = f32(c)[np.ix_(rows_x, rows_w)]
