@@ -44,9 +44,9 @@ PEAK_BY_ACCUM = {"exact": PEAK_FP16_TFLOPS, "mfma_fp8": PEAK_FP8_TFLOPS}
 # the same counter reads for a 256 MiB device copy (profiles/gemm_fc1_8192x16384x4096_hbm_traffic.md).  Valid
 # only for the kernel sources they were taken on: GEMM_SOURCES hashed in order must give GEMM_TRAFFIC_SHA256.
 GEMM_SOURCES = ("gemm.hip", "gemm_dispatch.hpp", "gemm_kernel.hpp", "gemm_tile.hpp", "device_common.hpp")
-GEMM_TRAFFIC_SHA256 = "d5df23936693a92d78fb5874cdb0806bc7695309e33f59ae9a250679b72f2c6c"
-GEMM_TRAFFIC = {"exact": {"read_bytes": 1243211971, "write_bytes": 268780480},
-                "mfma_fp8": {"read_bytes": 1209496637, "write_bytes": 271124331}}
+GEMM_TRAFFIC_SHA256 = "692ae391df279db82ac34d2ca5fb7990eba75ab317e6d1329237856bd74faf13"
+GEMM_TRAFFIC = {"exact": {"read_bytes": 1260498016, "write_bytes": 268716096},
+                "mfma_fp8": {"read_bytes": 1209374443, "write_bytes": 271599296}}
 
 
 def gemm_traffic(accum):
