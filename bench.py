@@ -534,7 +534,7 @@ def vendor_reference(torch, iters=20):
     return out
 
 
-def cpu_baseline(rows=512):
+def cpu_baseline(rows=4096):
     """The CPU oracle on a bounded slice of the headline step: delayed-scaled cast
     of `rows` rows of X, cast of the whole W, and the dequantised GEMM of those
     rows (fp64 BLAS).  Reported in TFLOP/s of the GEMM FLOPs of the slice."""
