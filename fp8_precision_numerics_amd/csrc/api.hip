@@ -65,7 +65,7 @@ const char* fp8mi_status_string(int status) {
   }
 }
 
-int fp8mi_version(void) { return 600; }
+int fp8mi_version(void) { return 700; }
 
 int fp8_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, const float* scale,
                  uint8_t* q, uint8_t* q_t, float* amax, unsigned long long* sat, void* workspace,
@@ -87,6 +87,29 @@ int fp8_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, 
   if (dev != FP8MI_OK) return dev;
   return launched(fp8mi::launch_quantize(x, xtype, rows, cols, fmt, scale, q, q_t, amax, sat, workspace,
                                          workspace_bytes, (hipStream_t)stream));
+}
+
+int fp8_quantize_update(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, uint8_t* q, uint8_t* q_t,
+                        float* amax, unsigned long long* sat, void* workspace, size_t workspace_bytes, float* history,
+                        int32_t history_len, int32_t* head, float* scale, float* scale_inv, int32_t* status,
+                        float* scale_inv_used, void* stream) {
+  if (!dtype_ok(xtype)) return FP8MI_ERR_DTYPE;
+  if (!fmt_ok(fmt)) return FP8MI_ERR_FORMAT;
+  if (!dims_ok(rows, cols)) return FP8MI_ERR_SHAPE;
+  if (history_len < 1 || history_len > 4096) return FP8MI_ERR_SHAPE;
+  const int64_t n = rows * cols;
+  if (!amax || !history || !head || !scale || !scale_inv) return FP8MI_ERR_NULL;
+  if (n > 0 && !x) return FP8MI_ERR_NULL;
+  if ((x && !aligned16(x)) || (q && !aligned16(q)) || (q_t && !aligned16(q_t))) return FP8MI_ERR_ALIGN;
+  if (q_t && ((rows & 15) || (cols & 15))) return FP8MI_ERR_ALIGN;
+  if (workspace && (!aligned16(workspace) || workspace_bytes < 16)) return FP8MI_ERR_ALIGN;
+  if (q_t && (rows + 127) / 128 > 65535) return FP8MI_ERR_SHAPE;
+  if ((cols + 127) / 128 > kMaxDim) return FP8MI_ERR_SHAPE;
+  const int dev = check_device();
+  if (dev != FP8MI_OK) return dev;
+  const fp8mi::HistoryArgs hs{history, history_len, head, scale, scale_inv, status, fmt, scale_inv_used};
+  return launched(fp8mi::launch_quantize(x, xtype, rows, cols, fmt, scale, q, q_t, amax, sat, workspace,
+                                         workspace_bytes, (hipStream_t)stream, hs));
 }
 
 int fp8_amax_update(float* history, int32_t history_len, int32_t* head, const float* amax, int fmt,

@@ -8,10 +8,24 @@
 
 namespace fp8mi {
 
+// The delayed-scaling history step a cast may run right after itself
+// (fp8_quantize_update); `history` null = none.
+struct HistoryArgs {
+  float* history;
+  int len;
+  int32_t* head;
+  float* scale;
+  float* scale_inv;
+  int32_t* status;
+  int fmt;
+  float* sinv_used;  // receives *scale_inv as it was before the step (may be null)
+};
+
 hipError_t launch_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt,
                            const float* scale, uint8_t* q, uint8_t* q_t, float* amax,
                            unsigned long long* sat, void* workspace, size_t workspace_bytes,
-                           hipStream_t stream);
+                           hipStream_t stream, HistoryArgs hs = HistoryArgs{nullptr, 0, nullptr, nullptr, nullptr,
+                                                                           nullptr, 0, nullptr});
 
 hipError_t launch_quantize_blockwise(const void* x, int xtype, int64_t rows, int64_t cols,
                                      int block_rows, int fmt, uint8_t* q, float* scale_inv,

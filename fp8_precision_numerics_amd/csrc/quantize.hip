@@ -68,12 +68,19 @@ __device__ __forceinline__ void block_finish(uint32_t amx, uint32_t wave_cnt, ui
   }
 }
 
-// Reduce `count` workgroup partials into the outputs (one workgroup).
+// Reduce `count` workgroup partials into the outputs (one workgroup) and,
+// when `hs.history` is set, run the delayed-scaling history step on the
+// reduced amax in the same launch (the rule of amax_update.hip: push it into
+// the ring at *head, advance the head, scale = MAX / max(ring) when that max
+// is finite and non-zero, else hold the scale and set status bit 0; a head
+// outside [0, len) is treated as 0 and sets status bit 1).
 __global__ __launch_bounds__(kThreads) void reduce_partials_kernel(const uint4* __restrict__ partials, int count,
                                                                   uint32_t* __restrict__ amax_bits,
-                                                                  unsigned long long* __restrict__ sat) {
+                                                                  unsigned long long* __restrict__ sat,
+                                                                  HistoryArgs hs) {
   __shared__ uint32_t s_max[kWaves];
   __shared__ unsigned long long s_cnt[kWaves];
+  __shared__ uint32_t s_amax;
   uint32_t m = 0u;
   unsigned long long c = 0ull;
   for (int i = threadIdx.x; i < count; i += kThreads) {
@@ -98,7 +105,47 @@ __global__ __launch_bounds__(kThreads) void reduce_partials_kernel(const uint4* 
     }
     if (amax_bits) *amax_bits = m;
     if (sat) *sat = c;
+    s_amax = m;
   }
+  if (!hs.history) return;  // uniform
+  __syncthreads();
+  const uint32_t a = s_amax;
+  int h = *hs.head;
+  int flags = 0;
+  if (h < 0 || h >= hs.len) {
+    h = 0;
+    flags |= 2;
+  }
+  uint32_t hm = 0u;
+  for (int i = threadIdx.x; i < hs.len; i += kThreads) {
+    const uint32_t b = (i == h) ? a : (f2u(hs.history[i]) & 0x7FFFFFFFu);
+    hm = hm > b ? hm : b;
+  }
+  hm = wave_max_u32(hm);
+  __syncthreads();  // s_max is reused
+  if (lane == 0) s_max[wave] = hm;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) hm = hm > s_max[w] ? hm : s_max[w];
+    if (hs.sinv_used) *hs.sinv_used = *hs.scale_inv;
+    hs.history[h] = u2f(a);
+    *hs.head = (h + 1 == hs.len) ? 0 : h + 1;
+    float sc, si;
+    const bool ok = hs.fmt == kE4M3 ? scale_from_amax_bits<kE4M3>(hm, &sc, &si) : scale_from_amax_bits<kE5M2>(hm, &sc, &si);
+    if (ok) {
+      *hs.scale = sc;
+      *hs.scale_inv = si;
+    } else {
+      flags |= 1;
+    }
+    if (hs.status && flags) *hs.status |= flags;
+  }
+}
+
+// One fp32 value copied on the device (stream-ordered, capturable).
+__global__ void copy_scalar_kernel(const float* __restrict__ src, float* __restrict__ dst) {
+  if (threadIdx.x == 0) *dst = *src;
 }
 
 // With a finite non-zero scale, x * s is NaN exactly where x is NaN.
@@ -529,7 +576,7 @@ void launch_blockwise_t(const void* x, int64_t rows, int64_t cols, int block_row
 hipError_t launch_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt,
                            const float* scale, uint8_t* q, uint8_t* q_t, float* amax,
                            unsigned long long* sat, void* workspace, size_t workspace_bytes,
-                           hipStream_t stream) {
+                           hipStream_t stream, HistoryArgs hs) {
   uint32_t* amax_bits = reinterpret_cast<uint32_t*>(amax);
   const bool reduce = amax_bits || sat;
   // With a workspace: per-workgroup partials, then one small reduction kernel.
@@ -544,8 +591,15 @@ hipError_t launch_quantize(const void* x, int xtype, int64_t rows, int64_t cols,
     else
       groups = launch_quantize_x<kF32>(x, rows, cols, fmt, scale, q, q_t, amax_bits, sat, partials, slots, stream);
   }
-  if (partials)
-    hipLaunchKernelGGL(reduce_partials_kernel, dim3(1), dim3(kThreads), 0, stream, partials, groups, amax_bits, sat);
+  if (partials) {
+    hipLaunchKernelGGL(reduce_partials_kernel, dim3(1), dim3(kThreads), 0, stream, partials, groups, amax_bits, sat,
+                       hs);
+  } else if (hs.history) {
+    if (hs.sinv_used) hipLaunchKernelGGL(copy_scalar_kernel, dim3(1), dim3(64), 0, stream, hs.scale_inv, hs.sinv_used);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_amax_update(hs.history, hs.len, hs.head, amax, hs.fmt, hs.scale, hs.scale_inv, hs.status, stream);
+  }
   return hipGetLastError();
 }
 

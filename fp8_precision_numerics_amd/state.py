@@ -48,6 +48,8 @@ class DelayedScalingState:
         self.scale_inv = torch.ones(1, dtype=torch.float32, device=dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         self.amax = torch.zeros(1, dtype=torch.float32, device=dev)
+        # inverse of the scale the last quantize_update cast with (the GEMM's factor for those codes)
+        self.scale_inv_used = torch.ones(1, dtype=torch.float32, device=dev)
         self.sat = torch.zeros(1, dtype=torch.int64, device=dev)
         # scratch for the per-workgroup partials of amax and the count
         self.workspace = torch.empty(_b.QUANTIZE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
@@ -55,6 +57,14 @@ class DelayedScalingState:
     def quantize(self, x, q=None, q_t=None, count_saturation=False, stream=None):
         _b.fp8_quantize(x, self.fmt, self.scale, q=q, q_t=q_t, amax=self.amax,
                         sat=self.sat if count_saturation else None, workspace=self.workspace, stream=stream)
+
+    def quantize_update(self, x, q=None, q_t=None, count_saturation=False, stream=None):
+        """quantize then update in one library call (the history step rides on the
+        launch that reduces the cast's partial amaxes).  Afterwards scale_inv
+        belongs to the next step; a GEMM on these codes takes scale_inv_used."""
+        _b.fp8_quantize_update(x, self.fmt, self.history, self.head, self.scale, self.scale_inv, self.amax, q=q,
+                               q_t=q_t, sat=self.sat if count_saturation else None, status=self.status,
+                               workspace=self.workspace, scale_inv_used=self.scale_inv_used, stream=stream)
 
     def update(self, stream=None):
         _b.fp8_amax_update(self.history, self.head, self.amax, self.fmt, self.scale, self.scale_inv,

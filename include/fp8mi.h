@@ -152,6 +152,29 @@ FP8MI_API int fp8_amax_update(float* history, int32_t history_len, int32_t* head
                     int fmt, float* scale, float* scale_inv, int32_t* status, void* stream);
 
 /*
+ * fp8_quantize_update — one delayed-scaling step of a tensor in one call
+ * ([TE] §4.2.4, §4.2.6: cast with the scale predicted from the history, then
+ * refresh the history and the scale for the next step): exactly
+ *     fp8_quantize(x, xtype, rows, cols, fmt, scale, q, q_t, amax, sat, workspace, workspace_bytes)
+ *     fp8_amax_update(history, history_len, head, amax, fmt, scale, scale_inv, status)
+ * in that order.  The cast uses *scale as it is on entry; the new scale is
+ * written after every element has been cast.  With a workspace, the history
+ * step runs inside the launch that reduces the per-workgroup partials (two
+ * launches in all instead of three).
+ *
+ * Arguments as for those two calls; amax is required here (it receives this
+ * step's amax, which is also pushed into the history).
+ * scale_inv_used  device, 1 fp32, or NULL: receives *scale_inv as it was on
+ *         entry, i.e. the inverse of the scale this cast used.  A GEMM that
+ *         consumes q must be given this value, not *scale_inv, which already
+ *         belongs to the next step.
+ */
+FP8MI_API int fp8_quantize_update(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, uint8_t* q,
+                        uint8_t* q_t, float* amax, unsigned long long* sat, void* workspace, size_t workspace_bytes,
+                        float* history, int32_t history_len, int32_t* head, float* scale, float* scale_inv,
+                        int32_t* status, float* scale_inv_used, void* stream);
+
+/*
  * fp8_gemm — FP8 x FP8 GEMM with FP32 accumulation and the x(1/scale) restore
  * in the epilogue ([TE] §4.2.4; [FMT] "Technical insight").
  *

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert fm.version() == 600
+    assert fm.version() == 700
     for code in (OK, ENULL, ESHAPE, EALIGN, EFMT, EDTYPE, ELAUNCH, EDEV, EACCUM):
         assert fm.status_string(code) and fm.status_string(code) != "unknown status"
     assert fm.status_string(12345) == "unknown status"
@@ -118,13 +118,26 @@ def test_mx_argument_errors(lib):
     assert gm(A16, 0, A16, A16, 0, A16, 16, 16, 1 << 24, A16, 0, None) == ESHAPE
 
 
+def test_quantize_update_argument_errors(lib):
+    u = lib.fp8_quantize_update
+    #        x   xt rows cols fmt q    qt    amax sat  ws   wsb hist  len head scale sinv status used stream
+    assert u(A16, 7, 4, 16, 0, A16, None, A16, None, None, 0, A16, 16, A16, A16, A16, None, None, None) == EDTYPE
+    assert u(A16, 0, 4, 16, 9, A16, None, A16, None, None, 0, A16, 16, A16, A16, A16, None, None, None) == EFMT
+    assert u(A16, 0, 4, 16, 0, A16, None, A16, None, None, 0, A16, 0, A16, A16, A16, None, None, None) == ESHAPE
+    assert u(A16, 0, 4, 16, 0, A16, None, None, None, None, 0, A16, 16, A16, A16, A16, None, None, None) == ENULL
+    assert u(A16, 0, 4, 16, 0, A16, None, A16, None, None, 0, None, 16, A16, A16, A16, None, None, None) == ENULL
+    assert u(A16, 0, 4, 16, 0, A16, None, A16, None, None, 0, A16, 16, A16, None, A16, None, None, None) == ENULL
+    assert u(A8, 0, 4, 16, 0, A16, None, A16, None, None, 0, A16, 16, A16, A16, A16, None, None, None) == EALIGN
+    assert u(A16, 0, 4, 24, 0, None, A16, A16, None, None, 0, A16, 16, A16, A16, A16, None, None, None) == EALIGN
+
+
 def test_amax_update_argument_errors(lib):
     u = lib.fp8_amax_update
-    assert u(A16, 16, A16, A16, 5, A16, A16, None, None) == EFMT
-    assert u(None, 16, A16, A16, 0, A16, A16, None, None) == ENULL
-    assert u(A16, 16, A16, A16, 0, None, A16, None, None) == ENULL
-    assert u(A16, 0, A16, A16, 0, A16, A16, None, None) == ESHAPE
-    assert u(A16, 4097, A16, A16, 0, A16, A16, None, None) == ESHAPE
+    assert u(A16, 16, A16, A16, 5, A16, A16, None, None, None) == EFMT
+    assert u(None, 16, A16, A16, 0, A16, A16, None, None, None) == ENULL
+    assert u(A16, 16, A16, A16, 0, None, A16, None, None, None) == ENULL
+    assert u(A16, 0, A16, A16, 0, A16, A16, None, None, None) == ESHAPE
+    assert u(A16, 4097, A16, A16, 0, A16, A16, None, None, None) == ESHAPE
 
 
 def test_gemm_argument_errors(lib):

@@ -17,7 +17,10 @@ def _state_arrays(st):
     return {k: getattr(st, k).detach().cpu().numpy().copy() for k in ("history", "head", "scale", "scale_inv", "amax", "sat")}
 
 
-def test_graph_replays_match_eager_delayed_scaling():
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_replays_match_eager_delayed_scaling(fused):
+    """fused: the graph holds fp8_quantize_update (cast and history step in one
+    call); the eager reference always runs the two separate calls."""
     dev = device()
     rng = np.random.default_rng(77)
     xs = [torch.from_numpy((rng.standard_normal((512, 1024)) * 3.0 ** t).astype(np.float32)).to(dev).to(torch.bfloat16)
@@ -37,10 +40,13 @@ def test_graph_replays_match_eager_delayed_scaling():
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for x in xs:
-            st.quantize(x, q=q_graph, count_saturation=True)
-            st.update()
+            if fused:
+                st.quantize_update(x, q=q_graph, count_saturation=True)
+            else:
+                st.quantize(x, q=q_graph, count_saturation=True)
+                st.update()
     for replay in range(3):
-        announce(f"graph replay {replay}")
+        announce(f"graph replay {replay} fused={fused}")
         graph.replay()
         for x in xs:                       # the same four steps, eagerly
             eager.quantize(x, q=q_eager, count_saturation=True)
