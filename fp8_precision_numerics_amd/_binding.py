@@ -42,7 +42,7 @@ def library_path() -> str:
 
 
 # Workspace size that lets a cast grid cover the device (FP8MI_QUANTIZE_WORKSPACE_BYTES).
-QUANTIZE_WORKSPACE_BYTES = 16384
+QUANTIZE_WORKSPACE_BYTES = 65536
 
 
 class Fp8Error(RuntimeError):

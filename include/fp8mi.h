@@ -114,13 +114,14 @@ FP8MI_API int fp8mi_version(void);
  *          one, each workgroup writes its partial amax / count into it and a
  *          small second kernel reduces them (no contended atomics); up to
  *          workspace_bytes / 16 workgroups are used, so FP8MI_QUANTIZE_WORKSPACE_BYTES
- *          lets the grid cover the device.  Contents on entry do not matter;
+ *          lets the grid cover the device (the cast-transpose keeps up to 8
+ *          workgroups per compute unit resident).  Contents on entry do not matter;
  *          two calls in flight at once must not share one workspace.  Without
  *          one, the outputs are cleared and then updated with atomics.
  * At least one of q, q_t, amax must be non-NULL.  rows*cols may be 0 (then
  * amax = 0 and sat = 0).
  */
-#define FP8MI_QUANTIZE_WORKSPACE_BYTES 16384
+#define FP8MI_QUANTIZE_WORKSPACE_BYTES 65536
 
 FP8MI_API int fp8_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt,
                  const float* scale, uint8_t* q, uint8_t* q_t, float* amax,
