@@ -74,6 +74,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--quick", action="store_true", help="headline step only (no extras, no CPU baseline)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--with-stream", action="store_true",
+                   help="with --quick: also run the 32-step delayed-scaling stream (for counter runs of the cast)")
     p.add_argument("--stream-dtype", default="bf16", choices=["bf16", "f32"])
     p.add_argument("--accum", default="exact", choices=["exact", "mfma_fp8"],
                    help="GEMM accumulation mode of the timed step (the other mode is timed as an extra)")
@@ -606,8 +608,9 @@ def main():
         torch.cuda.synchronize()
         extra["copy_calibration_bytes"] = src.numel()
         del src, dst
-    if not args.quick:
+    if not args.quick or args.with_stream:
         extra["stream"] = stream_bench(torch, fm, args.stream_dtype)
+    if not args.quick:
         extra["linear_step"] = linear_bench(torch, fm)
         extra["moe_grouped"] = moe_bench(torch, fm)
         extra["grad_allreduce_parts"] = allreduce_bench(torch, fm)
