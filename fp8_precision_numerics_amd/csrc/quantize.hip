@@ -190,23 +190,38 @@ __device__ __forceinline__ void store_nt(uint8_t* __restrict__ q, int64_t vi, ui
   __builtin_nontemporal_store(c0, reinterpret_cast<uint32_t*>(q) + vi);
 }
 
+// A 16-B input vector as fp32 values (exact widening of bf16).
+template <int XT>
+__device__ __forceinline__ void widen_vec(const uint4& a, float* v) {
+  if constexpr (XT == kBF16) {
+    v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+    v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+  } else {
+    v[0] = u2f(a.x); v[1] = u2f(a.y); v[2] = u2f(a.z); v[3] = u2f(a.w);
+  }
+}
+
+// The largest magnitude bit pattern of a 16-B input vector, as fp32 bits.
+template <int XT>
+__device__ __forceinline__ uint32_t vec_max_bits(const uint4& a) {
+  if constexpr (XT == kBF16) {
+    const us2 m0 = __builtin_bit_cast(us2, a.x & 0x7FFF7FFFu), m1 = __builtin_bit_cast(us2, a.y & 0x7FFF7FFFu);
+    const us2 m2 = __builtin_bit_cast(us2, a.z & 0x7FFF7FFFu), m3 = __builtin_bit_cast(us2, a.w & 0x7FFF7FFFu);
+    const us2 m = __builtin_elementwise_max(__builtin_elementwise_max(m0, m1), __builtin_elementwise_max(m2, m3));
+    return (uint32_t)(m[0] > m[1] ? m[0] : m[1]) << 16;
+  } else {
+    const uint32_t m01 = (a.x & 0x7FFFFFFFu) > (a.y & 0x7FFFFFFFu) ? (a.x & 0x7FFFFFFFu) : (a.y & 0x7FFFFFFFu);
+    const uint32_t m23 = (a.z & 0x7FFFFFFFu) > (a.w & 0x7FFFFFFFu) ? (a.z & 0x7FFFFFFFu) : (a.w & 0x7FFFFFFFu);
+    return m01 > m23 ? m01 : m23;
+  }
+}
+
 // Load vector `vi` as fp32 values and the max of its magnitude bit patterns.
 template <int XT, bool NT = false>
 __device__ __forceinline__ void load_vec(const void* __restrict__ x, int64_t vi, float* v, uint32_t& vmax) {
   const uint4 a = load16<NT>(x, vi);
-  if constexpr (XT == kBF16) {
-    v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
-    v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
-    const us2 m0 = __builtin_bit_cast(us2, a.x & 0x7FFF7FFFu), m1 = __builtin_bit_cast(us2, a.y & 0x7FFF7FFFu);
-    const us2 m2 = __builtin_bit_cast(us2, a.z & 0x7FFF7FFFu), m3 = __builtin_bit_cast(us2, a.w & 0x7FFF7FFFu);
-    const us2 m = __builtin_elementwise_max(__builtin_elementwise_max(m0, m1), __builtin_elementwise_max(m2, m3));
-    vmax = (uint32_t)(m[0] > m[1] ? m[0] : m[1]) << 16;
-  } else {
-    v[0] = u2f(a.x); v[1] = u2f(a.y); v[2] = u2f(a.z); v[3] = u2f(a.w);
-    const uint32_t m01 = (a.x & 0x7FFFFFFFu) > (a.y & 0x7FFFFFFFu) ? (a.x & 0x7FFFFFFFu) : (a.y & 0x7FFFFFFFu);
-    const uint32_t m23 = (a.z & 0x7FFFFFFFu) > (a.w & 0x7FFFFFFFu) ? (a.z & 0x7FFFFFFFu) : (a.w & 0x7FFFFFFFu);
-    vmax = m01 > m23 ? m01 : m23;
-  }
+  widen_vec<XT>(a, v);
+  vmax = vec_max_bits<XT>(a);
 }
 
 template <int XT>
@@ -388,18 +403,27 @@ __global__ __launch_bounds__(kThreads) void quantize_transpose_kernel(
   // Persistent grid: each workgroup walks tiles blockIdx.x, +gridDim.x, ...
   for (int64_t tile_id = blockIdx.x; tile_id < tiles; tile_id += gridDim.x) {
   const int64_t row0 = (tile_id / tiles_c) * kTile, col0 = (tile_id % tiles_c) * kTile;
-  float v[PASSES][EPV];
+  // Raw 16-B vectors (widened one pass at a time, which keeps the register
+  // footprint, and with it the occupancy, down) and their magnitude maxima.
+  uint4 raw[PASSES];
   uint32_t vm[PASSES];
-  auto cast_pass = [&](int i) {
+  auto cast_pass = [&](int i, bool in_range) {
     const int rr = rr0 + i * RPP;
     const int64_t r = row0 + rr, c = col0 + vi * EPV;
-    amx = amx > vm[i] ? amx : vm[i];
-    const bool finite = regular && vm[i] <= 0x7F800000u;
-    const uint32_t c0 = scale_encode4<FMT, SAT>(&v[i][0], s, finite, wcnt);
+    float v[EPV];
+    widen_vec<XT>(raw[i], v);
+    uint32_t c0, c1 = 0u;
+    if (in_range) {
+      c0 = scale_encode4_inrange<FMT>(&v[0], s);
+      if constexpr (EPV == 8) c1 = scale_encode4_inrange<FMT>(&v[4], s);
+    } else {
+      const bool finite = regular && vm[i] <= 0x7F800000u;
+      c0 = scale_encode4<FMT, SAT>(&v[0], s, finite, wcnt);
+      if constexpr (EPV == 8) c1 = scale_encode4<FMT, SAT>(&v[4], s, finite, wcnt);
+    }
     uint32_t* dst = reinterpret_cast<uint32_t*>(tile + rr * kPitch + vi * EPV);
     dst[0] = c0;
     if constexpr (EPV == 8) {
-      const uint32_t c1 = scale_encode4<FMT, SAT>(&v[i][4], s, finite, wcnt);
       dst[1] = c1;
       if constexpr (WQ) *reinterpret_cast<uint2*>(q + r * cols + c) = make_uint2(c0, c1);
     } else {
@@ -407,23 +431,37 @@ __global__ __launch_bounds__(kThreads) void quantize_transpose_kernel(
     }
   };
   if (row0 + kTile <= rows && col0 + kTile <= cols) {
-    // Interior tile: every load issued before any use.
+    // Interior tile: every load issued before any use; when no product of the
+    // wave's part of the tile can exceed max, the clamp, the count and the NaN
+    // rule are no-ops (as in the flat cast).
 #pragma unroll
     for (int i = 0; i < PASSES; ++i)
-      load_vec<XT>(x, (row0 + rr0 + i * RPP) * vecs_per_row + (col0 + vi * EPV) / EPV, v[i], vm[i]);
+      raw[i] = load16<false>(x, (row0 + rr0 + i * RPP) * vecs_per_row + (col0 + vi * EPV) / EPV);
+    uint32_t cm = 0u;
 #pragma unroll
-    for (int i = 0; i < PASSES; ++i) cast_pass(i);
+    for (int i = 0; i < PASSES; ++i) {
+      vm[i] = vec_max_bits<XT>(raw[i]);
+      cm = cm > vm[i] ? cm : vm[i];
+    }
+    amx = amx > cm ? amx : cm;
+    const bool in_range = __builtin_amdgcn_ballot_w64(!chunk_in_range<FMT>(cm, s)) == 0;
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) cast_pass(i, in_range);
   } else {
 #pragma unroll
     for (int i = 0; i < PASSES; ++i) {
       const int64_t r = row0 + rr0 + i * RPP, c = col0 + vi * EPV;
-      vm[i] = 0u;
-      if (r < rows && c < cols) load_vec<XT>(x, r * vecs_per_row + c / EPV, v[i], vm[i]);
+      raw[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (r < rows && c < cols) raw[i] = load16<false>(x, r * vecs_per_row + c / EPV);
+      vm[i] = vec_max_bits<XT>(raw[i]);
     }
 #pragma unroll
     for (int i = 0; i < PASSES; ++i) {
       const int64_t r = row0 + rr0 + i * RPP, c = col0 + vi * EPV;
-      if (r < rows && c < cols) cast_pass(i);
+      if (r < rows && c < cols) {
+        amx = amx > vm[i] ? amx : vm[i];
+        cast_pass(i, false);
+      }
     }
   }
   __syncthreads();

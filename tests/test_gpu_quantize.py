@@ -98,6 +98,85 @@ def test_shapes_rowmajor_and_transpose(shape, fmt, dtype, wsp):
     assert int(sat.item()) == ws and ws > 0
 
 
+@pytest.mark.parametrize("wsp", [None, "full"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_chunk_gated_cast_at_its_boundaries(fmt, dtype, wsp):
+    """The flat cast skips the clamp, the saturation count and the NaN rule for a
+    wave's chunk (64 lanes x 4 vectors of 16 B) whose largest |x| times the scale
+    is at most max.  Plant, in separate chunks of otherwise small values: a
+    product exactly at max, the next value above it, a NaN, -Inf, -0 with
+    subnormal-range values, -max; then a saturating value in the partial last
+    chunk and a NaN in the ragged tail.  Every code, amax and count must match
+    the oracle for several scales, including a negative one."""
+    fmax = codec.FORMATS[fmt].max_value
+    epv = 8 if dtype == "bf16" else 4
+    ch = 64 * 4 * epv                                   # elements per wave chunk
+    n = 40 * ch + ch // 2 + 5                           # full chunks, a partial chunk, a ragged tail
+    rng = np.random.default_rng(71 + FMTS.index(fmt) * 2 + (dtype == "bf16"))
+    x = rng.uniform(-50.0, 50.0, n).astype(np.float32)
+    edge = np.float32(fmax / 2.0)                       # x * 2 == max exactly
+    above = np.nextafter(edge, np.float32(np.inf), dtype=np.float32)
+    if dtype == "bf16":                                 # the next bf16 above max / 2
+        above = np.float32(edge + np.float32(2.0 ** (np.floor(np.log2(edge)) - 7)))
+    plant = {1: edge, 2: above, 3: np.float32(np.nan), 4: np.float32(-np.inf), 7: -edge}
+    for c, v in plant.items():
+        x[c * ch + 137 + 11 * c] = v
+    x[5 * ch:6 * ch] = rng.uniform(-1e-9, 1e-9, ch).astype(np.float32)
+    x[5 * ch + 3] = np.float32(-0.0)
+    x[40 * ch + 300] = above                            # in the partial last chunk
+    x[n - 2] = np.float32(np.nan)                       # in the ragged tail
+    h = HostTensor(x, "f32") if dtype == "f32" else HostTensor(bf16_bits_from_f32(x), "bf16")
+    xw = scaling.widen(h.data, dtype)
+    assert xw[1 * ch + 148] == edge and xw[2 * ch + 159] == above
+    xd = to_device(h)
+    for s in (2.0, -2.0, 3.0, 2.0 ** -30):
+        announce(f"chunk-gated cast fmt={fmt} dtype={dtype} n={n} scale={s} workspace={wsp}")
+        q, _, amax, sat = gpu_quantize(xd, fmt, s, ws=wsp)
+        wq, wa, ws = oracle_quantize(xw, fmt, s)
+        bad = np.flatnonzero(u8(q) != wq)
+        assert bad.size == 0, [(int(i), float(xw[i]), hex(int(u8(q)[i])), hex(int(wq[i]))) for i in bad[:6]]
+        assert np.isnan(amax.item()) and np.isnan(wa)
+        assert int(sat.item()) == ws
+    # the planted boundary values on their own: exactly max is not saturated, the next value is
+    _, _, ws2 = oracle_quantize(xw, fmt, 2.0)
+    assert ws2 == 3                                     # above (twice) and -Inf
+
+
+def test_workspace_reuse_across_calls_and_sizes():
+    """One workspace reused for flat casts and cast-transposes of different
+    sizes (different grids, so different numbers of partials), starting from
+    random junk, with calls that see only 16 or 40 bytes of it (one and two
+    workgroups); every call must match the oracle: the partials of earlier
+    calls never leak into later ones."""
+    dev = device()
+    rng = np.random.default_rng(23)
+    ws = torch.from_numpy(rng.integers(0, 256, fm.QUANTIZE_WORKSPACE_BYTES, dtype=np.uint8)).to(dev)
+    shapes = [(512, 4096), (64, 48), (2048, 1024), (1, 1000003), (512, 4096), (4096, 256)]
+    for i, shape in enumerate(shapes):
+        x32 = (rng.standard_normal(shape) * 10.0 ** rng.uniform(-1, 2)).astype(np.float32)
+        h = HostTensor(bf16_bits_from_f32(x32), "bf16")
+        xw = scaling.widen(h.data, "bf16")
+        xd = to_device(h, dev)
+        s = float(scaling.scale_from_amax(scaling.amax(xw) * np.float32(0.8), 448.0)[1])
+        view = ws[:16] if i == 2 else (ws[:40] if i == 4 else ws)
+        tr = shape[0] % 16 == 0 and shape[1] % 16 == 0
+        announce(f"workspace reuse call {i} shape {shape} workspace {view.numel()} B transpose={tr}")
+        st = torch.tensor([s], dtype=torch.float32, device=dev)
+        q = torch.empty(shape, dtype=torch.uint8, device=dev)
+        qt = torch.empty((shape[1], shape[0]), dtype=torch.uint8, device=dev) if tr else None
+        amax = torch.full((1,), -1.0, dtype=torch.float32, device=dev)
+        sat = torch.full((1,), 12345, dtype=torch.int64, device=dev)
+        fm.fp8_quantize(xd, "e4m3", st, q=q, q_t=qt, amax=amax, sat=sat, workspace=view)
+        torch.cuda.synchronize()
+        wq, wa, wsat = oracle_quantize(xw, "e4m3", s)
+        assert np.array_equal(u8(q).reshape(shape), wq.reshape(shape))
+        if tr:
+            assert np.array_equal(u8(qt).reshape(shape[1], shape[0]), wq.reshape(shape).T)
+        assert bits32(amax)[0] == np.float32(wa).view(np.uint32)
+        assert int(sat.item()) == wsat and wsat > 0
+
+
 def test_transpose_only_and_amax_only():
     rng = np.random.default_rng(5)
     x32 = rng.standard_normal((256, 512)).astype(np.float32)
