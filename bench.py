@@ -13,7 +13,7 @@ Inputs are synthetic (seeded), resident in HBM before timing starts.
 Printed on stdout: ONE JSON line.  `value` is GEMM FLOP / step time (TFLOP/s
 of the whole step); `roofline` is the GEMM kernel alone (HIP events around
 each launch on its stream); `extra` holds the delayed-scaling stream
-(32 x 8192x4096, HBM GB/s of the fused amax+cast), one HYBRID linear-layer
+(32 x 8192x4096, bf16 and fp32 inputs, HBM GB/s of the fused amax+cast), one HYBRID linear-layer
 training step at the FC1 shape (forward, dgrad, wgrad, each launch timed), the
 fine-grained MoE grouped GEMM, one GPU's parts of an E5M2 gradient all-reduce,
 MXFP8 (block-32 quantisation and the block-scaled GEMM) on the FC1 shape, and
@@ -361,7 +361,23 @@ def linear_bench(torch, fm, iters=10):
         log(f"linear step ({accum}): {step_us:.1f} us = {r['step_tflops']:.0f} TFLOP/s; "
             + ", ".join(f"{k} {v:.1f}" for k, v in us.items()))
         res[accum] = r
-        del layer
+    # Gradients mix very large and very small magnitudes: the share of dY's
+    # (nonzero) entries that its E5M2 cast flushes to +-0, against a cast of the
+    # same tensor to E4M3 with E4M3's scale from the same amax history (what
+    # choosing E4M3 for gradients would lose).  Reporting only, after the timing.
+    sg = layer.state_g
+    hist_max = float(sg.history.max().item())
+    s4 = torch.tensor([448.0 / hist_max], dtype=torch.float32, device=dev)
+    q4 = torch.empty((T, O), dtype=torch.uint8, device=dev)
+    fm.fp8_quantize(G, "e4m3", s4, q=q4)
+    nonzero = G != 0
+    n_nz = int(nonzero.sum().item())
+    f5 = int((((layer.qg & 0x7F) == 0) & nonzero).sum().item()) / n_nz
+    f4 = int((((q4 & 0x7F) == 0) & nonzero).sum().item()) / n_nz
+    res["dy_flushed_to_zero"] = {"e5m2": f5, "e4m3_same_history": f4, "scale_e5m2": float(sg.scale.item()),
+                                 "scale_e4m3": float(s4.item()), "nonzero_entries": n_nz}
+    log(f"dY [{T}x{O}] entries flushed to 0: E5M2 {f5 * 100:.3f} %, E4M3 with the same history {f4 * 100:.3f} %")
+    del q4, nonzero, layer
     del G, W, X, Y, dX, dW
     torch.cuda.empty_cache()
     return res
@@ -611,6 +627,9 @@ def main():
         del src, dst
     if not args.quick or args.with_stream:
         extra["stream"] = stream_bench(torch, fm, args.stream_dtype)
+    if not args.quick:
+        other = "f32" if args.stream_dtype == "bf16" else "bf16"
+        extra["stream_" + other] = stream_bench(torch, fm, other)
     if not args.quick:
         extra["linear_step"] = linear_bench(torch, fm)
         extra["moe_grouped"] = moe_bench(torch, fm)
