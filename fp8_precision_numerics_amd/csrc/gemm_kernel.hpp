@@ -53,6 +53,7 @@ struct MxScales {
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;
+constexpr int kSchedValu = 0x002;
 constexpr int kSchedDsRead = 0x100;
 
 // dword 3 of a raw (untyped, stride 0) buffer resource on gfx9: 32-bit data format.
@@ -565,7 +566,23 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
       for (int i = 0; i < FM; ++i) ar[i][c] = granule(st, wm * WTM + i * 32, 4 * hh + c);
     };
     auto load_frags = [&](const uint8_t* st) { read_granule(st, 0); };
+    // The wave issues in order, so conversions written after a sub-step's
+    // MFMAs wait until the last of them has issued: with all 32 conversions of
+    // a sub-step ahead of its 16 MFMAs the matrix core idled while the next
+    // sub-step was being converted.  Here the B operands are converted one
+    // sub-step ahead, and the scheduling groups place two conversions (the
+    // remaining A blocks', then the next sub-step's B blocks') after each
+    // MFMA, inside its shadow (2-3 % faster on FC1, identical results).
+    auto cvt_b = [&](int s, v8h* out) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const uint4 g = br[j][s >> 1];
+        out[j] = (s & 1) ? widen8<FB>(g.z, g.w) : widen8<FB>(g.x, g.y);
+      }
+    };
     auto compute = [&](const uint8_t* st, auto&& dma) {
+      v8h bb[2][FN];
+      cvt_b(0, bb[0]);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         if (s < kDmaGroups) dma(s);
@@ -573,12 +590,7 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
           read_granule(st, (s >> 1) + 1);
           __builtin_amdgcn_sched_barrier(0);
         }
-        v8h bh[FN];
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const uint4 g = br[j][s >> 1];
-          bh[j] = (s & 1) ? widen8<FB>(g.z, g.w) : widen8<FB>(g.x, g.y);
-        }
+        const v8h* bh = bb[s & 1];
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           const uint4 g = ar[i][s >> 1];
@@ -586,7 +598,14 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
 #pragma unroll
           for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bh[j], ah, acc[i][j], 0, 0, 0);
         }
-        if (s & 1) __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 < 8) cvt_b(s + 1, bb[(s + 1) & 1]);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+#pragma unroll
+        for (int k = 0; k < FM * FN; ++k) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedValu, 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     auto interleave = [&]() {};

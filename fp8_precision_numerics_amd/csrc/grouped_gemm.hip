@@ -35,8 +35,6 @@
 namespace fp8mi {
 namespace {
 
-constexpr int kSchedValu = 0x002;
-
 // Output tiles of BM rows are laid end to end over the experts' row intervals
 // [m_offsets[g], m_offsets[g+1]) (made non-decreasing and clamped to
 // [0, total_m]).  Finds the expert of M tile `mt` and the tile's first row and
