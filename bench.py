@@ -44,9 +44,9 @@ PEAK_BY_ACCUM = {"exact": PEAK_FP16_TFLOPS, "mfma_fp8": PEAK_FP8_TFLOPS}
 # the same counter reads for a 256 MiB device copy (profiles/gemm_fc1_8192x16384x4096_hbm_traffic.md).  Valid
 # only for the kernel sources they were taken on: GEMM_SOURCES hashed in order must give GEMM_TRAFFIC_SHA256.
 GEMM_SOURCES = ("gemm.hip", "gemm_dispatch.hpp", "gemm_kernel.hpp", "gemm_tile.hpp", "device_common.hpp")
-GEMM_TRAFFIC_SHA256 = "434883bd384b232c3f9683bcd4030555be8d9afe0fcbbe0ff0dde4396b66259e"
-GEMM_TRAFFIC = {"exact": {"read_bytes": 1385727040, "write_bytes": 268499488},
-                "mfma_fp8": {"read_bytes": 1209505237, "write_bytes": 271612459}}
+GEMM_TRAFFIC_SHA256 = "6eb515db4316dd64d100181c98271a04ec39e629019c6f29c92e3cb2ce275124"
+GEMM_TRAFFIC = {"exact": {"read_bytes": 1214580384, "write_bytes": 269280832},
+                "mfma_fp8": {"read_bytes": 1209473899, "write_bytes": 271539925}}
 
 
 def gemm_traffic(accum):
