@@ -143,6 +143,43 @@ def test_chunk_gated_cast_at_its_boundaries(fmt, dtype, wsp):
     assert ws2 == 3                                     # above (twice) and -Inf
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_tile_gated_cast_transpose_at_its_boundaries(fmt, dtype):
+    """The cast-transpose skips the clamp, the count and the NaN rule for a
+    wave's part of a 128x128 tile whose largest |x| times the scale is at most
+    max.  Plant one boundary value per tile of a 3x4-tile tensor (plus a ragged
+    edge of 16 rows and 16 columns): a product exactly at max, the next value
+    above it, a NaN, -Inf, -max, and a tile of subnormal-range values with a -0;
+    both layouts, amax and count must match the oracle."""
+    fmax = codec.FORMATS[fmt].max_value
+    rows, cols = 3 * 128 + 16, 4 * 128 + 16
+    rng = np.random.default_rng(91 + FMTS.index(fmt) * 2 + (dtype == "bf16"))
+    x = rng.uniform(-50.0, 50.0, (rows, cols)).astype(np.float32)
+    edge = np.float32(fmax / 2.0)
+    above = np.nextafter(edge, np.float32(np.inf), dtype=np.float32)
+    if dtype == "bf16":
+        above = np.float32(edge + np.float32(2.0 ** (np.floor(np.log2(edge)) - 7)))
+    plant = {(0, 0): edge, (0, 1): above, (1, 2): np.float32(np.nan), (2, 3): np.float32(-np.inf),
+             (1, 0): -edge, (3, 4): above}                   # (3, 4): the ragged corner
+    for (tr, tc), v in plant.items():
+        x[tr * 128 + min(37 + tr, rows - tr * 128 - 1), tc * 128 + min(61 + tc, cols - tc * 128 - 1)] = v
+    x[128:256, 384:512] = rng.uniform(-1e-9, 1e-9, (128, 128)).astype(np.float32)
+    x[130, 400] = np.float32(-0.0)
+    h = HostTensor(x, "f32") if dtype == "f32" else HostTensor(bf16_bits_from_f32(x), "bf16")
+    xw = scaling.widen(h.data, dtype)
+    xd = to_device(h)
+    for s in (2.0, -2.0, 3.0):
+        announce(f"tile-gated cast-transpose fmt={fmt} dtype={dtype} {rows}x{cols} scale={s}")
+        q, qt, amax, sat = gpu_quantize(xd, fmt, s, transpose=True, ws="full")
+        wq, wa, ws = oracle_quantize(xw, fmt, s)
+        assert np.array_equal(u8(q).reshape(rows, cols), wq.reshape(rows, cols))
+        assert np.array_equal(u8(qt).reshape(cols, rows), wq.reshape(rows, cols).T)
+        assert np.isnan(amax.item()) and np.isnan(wa)
+        assert int(sat.item()) == ws
+    assert oracle_quantize(xw, fmt, 2.0)[2] == 3                 # above (twice) and -Inf
+
+
 def test_workspace_reuse_across_calls_and_sizes():
     """One workspace reused for flat casts and cast-transposes of different
     sizes (different grids, so different numbers of partials), starting from
