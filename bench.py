@@ -44,9 +44,9 @@ PEAK_BY_ACCUM = {"exact": PEAK_FP16_TFLOPS, "mfma_fp8": PEAK_FP8_TFLOPS}
 # the same counter reads for a 256 MiB device copy (profiles/gemm_fc1_8192x16384x4096_hbm_traffic.md).  Valid
 # only for the kernel sources they were taken on: GEMM_SOURCES hashed in order must give GEMM_TRAFFIC_SHA256.
 GEMM_SOURCES = ("gemm.hip", "gemm_dispatch.hpp", "gemm_kernel.hpp", "gemm_tile.hpp", "device_common.hpp")
-GEMM_TRAFFIC_SHA256 = "6eb515db4316dd64d100181c98271a04ec39e629019c6f29c92e3cb2ce275124"
-GEMM_TRAFFIC = {"exact": {"read_bytes": 1214580384, "write_bytes": 269280832},
-                "mfma_fp8": {"read_bytes": 1209473899, "write_bytes": 271539925}}
+GEMM_TRAFFIC_SHA256 = "b8d51dcccc202273efcefbad27558ebc4af9b1f98e2863675237c33c5f3b53cc"
+GEMM_TRAFFIC = {"exact": {"read_bytes": 1208493760, "write_bytes": 268521792},
+                "mfma_fp8": {"read_bytes": 1208714155, "write_bytes": 268881813}}
 
 
 def gemm_traffic(accum):

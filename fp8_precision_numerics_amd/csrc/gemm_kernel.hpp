@@ -27,6 +27,8 @@
 
 namespace fp8mi {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // Output kinds of the epilogue besides fp32 and bf16 (kF32, kBF16): FP8 codes
 // of the result re-quantised with a caller-supplied scale.
 enum : int { kOutE4M3 = 2, kOutE5M2 = 3 };
@@ -250,7 +252,14 @@ struct TileWriter {
       const uint4 v = *reinterpret_cast<const uint4*>(lds + pos(r, q * 16));
       uint8_t* dst = reinterpret_cast<uint8_t*>(C) + (m * N + n0) * CB + q * 16;
       if (full_cols) {
-        *reinterpret_cast<uint4*>(dst) = v;
+        // Nontemporal: the output is not read again by this kernel, and
+        // streaming it past the caches made the FC1 GEMM 5 % faster on MI355X.
+        u32x4 vv;
+        vv[0] = v.x;
+        vv[1] = v.y;
+        vv[2] = v.z;
+        vv[3] = v.w;
+        __builtin_nontemporal_store(vv, reinterpret_cast<u32x4*>(dst));
       } else {
         const uint8_t* src = reinterpret_cast<const uint8_t*>(&v);
         const int64_t nq = n0 + q * (16 / CB);
