@@ -56,15 +56,20 @@ __device__ __forceinline__ v4f decode4(uint32_t w) {
   return (v4f){lo[0], lo[1], hi[0], hi[1]};
 }
 
+typedef unsigned int ds_u2 __attribute__((ext_vector_type(2)));
+
+// Four consecutive outputs, one 16-byte (fp32) or 8-byte (bf16) nontemporal store.
 template <int OUT>
-__device__ __forceinline__ void store_out(void* out, int64_t i, const v4f& v) {
+__device__ __forceinline__ void store_out4(void* out, int64_t i, const v4f& v) {
   if constexpr (OUT == kF32) {
-    *reinterpret_cast<v4f*>(reinterpret_cast<float*>(out) + i) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(reinterpret_cast<float*>(out) + i));
   } else {
     const v2bf lo = __builtin_convertvector((v2f){v[0], v[1]}, v2bf);
     const v2bf hi = __builtin_convertvector((v2f){v[2], v[3]}, v2bf);
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + i) =
-        make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+    ds_u2 w;
+    w[0] = __builtin_bit_cast(uint32_t, lo);
+    w[1] = __builtin_bit_cast(uint32_t, hi);
+    __builtin_nontemporal_store(w, reinterpret_cast<ds_u2*>(reinterpret_cast<uint16_t*>(out) + i));
   }
 }
 
@@ -78,58 +83,69 @@ __device__ __forceinline__ void store_out1(void* out, int64_t i, float v) {
   }
 }
 
+// The four codes at p, of which the first `m` lie inside the payload (m <= 0:
+// none); codes past the end read as 0 and are never stored.
+__device__ __forceinline__ uint32_t load_codes4(const uint8_t* p, int64_t m) {
+  if (m >= 4) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  uint32_t w = 0;
+  for (int j = 0; j < m; ++j) w |= (uint32_t)p[j] << (8 * j);
+  return w;
+}
+
 // out[i] = fp32(fp32(sum over r = 0..R-1, in that order, of dec(q[r*stride + i])) * scale_inv).
-// Each thread takes 16 consecutive elements per grid-stride step: one 16-byte
-// load per rank (a batch of up to kBatch ranks in flight at once), 16 fp32
-// accumulators, one 64-byte (fp32) or 32-byte (bf16) store.
-constexpr int kBatch = 8;
+// A wave takes chunks of 1024 consecutive elements: four pieces 256 elements
+// apart, four elements per lane and piece.  Every load is then one 4-byte word
+// per lane and rank (256 contiguous bytes per wave) and every store 16 (fp32)
+// or 8 (bf16) contiguous bytes per lane, contiguous across the wave; up to
+// kBatch ranks' words are in flight at once, all accesses nontemporal (each
+// byte is touched once).  Sixteen consecutive elements per lane (one 16-byte
+// load per rank) ran 22 % slower on MI355X: each of its 16-byte stores
+// covered only a quarter of the 64 bytes between neighbouring lanes.
+constexpr int kBatch = 8, kChunk = 1024;
 
 template <int FMT, int OUT>
 __global__ __launch_bounds__(256) void dequant_sum_kernel(const uint8_t* __restrict__ q, int R, int64_t n,
                                                           int64_t stride, const float* __restrict__ scale_inv,
                                                           void* __restrict__ out) {
   const float si = scale_inv[0];
-  const int64_t nv = n >> 4;  // whole 16-element vectors
-  const int64_t step = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nv; v += step) {
-    const uint8_t* base = q + (v << 4);
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  const int64_t nchunks = (n + kChunk - 1) / kChunk;
+  for (int64_t c = wave; c < nchunks; c += nwaves) {
+    const int64_t e0 = c * kChunk + lane * 4;  // piece k covers [e0 + 256k, e0 + 256k + 4)
     v4f acc[4];
     for (int r0 = 0; r0 < R; r0 += kBatch) {
-      uint4 w[kBatch];
+      uint32_t w[kBatch][4];
 #pragma unroll
-      for (int b = 0; b < kBatch; ++b)
-        if (r0 + b < R) w[b] = *reinterpret_cast<const uint4*>(base + (int64_t)(r0 + b) * stride);
+      for (int b = 0; b < kBatch; ++b) {
+        if (r0 + b < R) {
+          const uint8_t* row = q + (int64_t)(r0 + b) * stride;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) w[b][k] = load_codes4(row + e0 + 256 * k, n - (e0 + 256 * k));
+        }
+      }
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
         if (r0 + b >= R) break;
-        const v4f d0 = decode4<FMT>(w[b].x), d1 = decode4<FMT>(w[b].y);
-        const v4f d2 = decode4<FMT>(w[b].z), d3 = decode4<FMT>(w[b].w);
-        if (r0 + b == 0) {
-          acc[0] = d0;
-          acc[1] = d1;
-          acc[2] = d2;
-          acc[3] = d3;
-        } else {
-          acc[0] += d0;
-          acc[1] += d1;
-          acc[2] += d2;
-          acc[3] += d3;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const v4f d = decode4<FMT>(w[b][k]);
+          acc[k] = r0 + b == 0 ? d : acc[k] + d;
         }
       }
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) store_out<OUT>(out, (v << 4) + 4 * k, acc[k] * si);
-  }
-  // ragged tail: the last n % 16 elements, one per thread of the first block
-  const int64_t tail0 = nv << 4;
-  if (blockIdx.x == 0 && tail0 + threadIdx.x < n) {
-    const int64_t i = tail0 + threadIdx.x;
-    float acc = 0.0f;
-    for (int r = 0; r < R; ++r) {
-      const float d = decode4<FMT>((uint32_t)q[(int64_t)r * stride + i])[0];
-      acc = r == 0 ? d : acc + d;
+    for (int k = 0; k < 4; ++k) {
+      const int64_t e = e0 + 256 * k;
+      const v4f o = acc[k] * si;
+      if (e + 4 <= n) {
+        store_out4<OUT>(out, e, o);
+      } else {
+        for (int j = 0; j < 4; ++j)
+          if (e + j < n) store_out1<OUT>(out, e + j, o[j]);
+      }
     }
-    store_out1<OUT>(out, i, acc * si);
   }
 }
 
@@ -137,8 +153,8 @@ template <int FMT, int OUT>
 hipError_t run_sum(const uint8_t* q, int R, int64_t n, int64_t stride, const float* si, void* out, hipStream_t st) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  const int64_t nv = n >> 4;
-  int64_t blocks = (nv + 255) / 256;
+  const int64_t nchunks = (n + kChunk - 1) / kChunk;
+  int64_t blocks = (nchunks + 3) / 4;  // four waves per workgroup, one chunk each
   const int64_t cap = (int64_t)cus * 8;
   blocks = blocks < 1 ? 1 : (blocks > cap ? cap : blocks);
   hipLaunchKernelGGL((dequant_sum_kernel<FMT, OUT>), dim3((unsigned)blocks), dim3(256), 0, st, q, R, n, stride, si,

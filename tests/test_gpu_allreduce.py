@@ -38,10 +38,13 @@ def _finite_codes(rng, shape, fmt):
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("R,n,pad", [(1, 1, 0), (2, 15, 16), (3, 17, 0), (8, 1000, 32), (9, 65541, 48),
-                                     (16, 4096, 0)])
+                                     (16, 4096, 0), (2, 8389635, 16)])
 def test_dequant_sum_bit_exact(R, n, pad, fmt, out):
     """Random finite codes over the whole range, payload rows padded to a
-    16-byte multiple (plus `pad`): fp32 sums in rank order, then x scale_inv."""
+    16-byte multiple (plus `pad`): fp32 sums in rank order, then x scale_inv.
+    The sizes cover a lone element, ragged ends inside a 4-element group and
+    inside a 1024-element wave chunk, more ranks than one batch of eight, and
+    (n = 8389635: 8194 chunks) more chunks than the launch has waves."""
     announce(f"dequant_sum R={R} n={n} {fmt} {out}")
     dev = device()
     rng = np.random.default_rng(R * 1000 + n)

@@ -30,7 +30,7 @@ def _special_rows(x):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
-@pytest.mark.parametrize("shape", [(1, 32), (5, 96), (130, 256), (300, 1024), (17, 4096)])
+@pytest.mark.parametrize("shape", [(1, 32), (5, 96), (130, 256), (300, 1024), (17, 4096), (128, 544)])
 def test_quantize_mx_bit_exact(shape, fmt, dtype):
     announce(f"quantize_mx {shape} {fmt} {dtype}")
     rng = np.random.default_rng(shape[0] * 31 + shape[1])
@@ -41,12 +41,42 @@ def test_quantize_mx_bit_exact(shape, fmt, dtype):
     xw = scaling.widen(h.data, dtype)
     dev = device()
     q = torch.empty(shape, dtype=torch.uint8, device=dev)
-    s = torch.empty((shape[1] // 32, fm.mx_scale_ld(shape[0])), dtype=torch.uint8, device=dev)
+    s = torch.full((shape[1] // 32, fm.mx_scale_ld(shape[0])), 0xA5, dtype=torch.uint8, device=dev)
     fm.fp8_quantize_mx(to_device(h, dev), fmt, q, s)
     torch.cuda.synchronize()
     wq, ws = mx.quantize_mx(xw, fmt)
-    assert np.array_equal(u8(s)[:, fm.mx_scale_pos(np.arange(shape[0]))].T, ws)   # K-block major, rows permuted
+    pos = fm.mx_scale_pos(np.arange(shape[0]))
+    assert np.array_equal(u8(s)[:, pos].T, ws)   # K-block major, rows permuted
     assert np.array_equal(u8(q), wq)
+    pad = np.ones(s.shape[1], dtype=bool)
+    pad[pos] = False
+    assert (u8(s)[:, pad] == 0xA5).all()          # positions of rows past the end are not written
+
+
+def test_quantize_mx_more_tiles_than_workgroups():
+    """8293 x 4128 bf16: 130 row groups x 9 block columns = 1170 tiles of 64
+    rows x 16 blocks, more than the 1024 workgroups launched, the last block
+    column one block wide and the last row group 37 rows: sampled rows from
+    every region (first pass, second pass, the cut group) bit for bit, and
+    the padding positions untouched."""
+    rows, cols = 8293, 4128
+    announce(f"quantize_mx {rows}x{cols} bf16 e4m3, sampled rows")
+    rng = np.random.default_rng(8293)
+    x = (rng.standard_normal((rows, cols)) * 10.0 ** rng.uniform(-3, 3, size=(rows, 1))).astype(np.float32)
+    h = HostTensor(bf16_bits_from_f32(x), "bf16")
+    dev = device()
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    s = torch.full((cols // 32, fm.mx_scale_ld(rows)), 0xA5, dtype=torch.uint8, device=dev)
+    fm.fp8_quantize_mx(to_device(h, dev), "e4m3", q, s)
+    torch.cuda.synchronize()
+    sample = np.unique(np.concatenate([[0, 63, 64, 7295, 8191, 8255, 8256, 8292],
+                                       rng.choice(rows, 24, replace=False)]))
+    wq, ws = mx.quantize_mx(scaling.widen(h.data[sample], "bf16"), "e4m3")
+    assert np.array_equal(u8(q)[sample], wq)
+    assert np.array_equal(u8(s)[:, fm.mx_scale_pos(sample)].T, ws)
+    pad = np.ones(s.shape[1], dtype=bool)
+    pad[fm.mx_scale_pos(np.arange(rows))] = False
+    assert pad.sum() == fm.mx_scale_ld(rows) - rows and (u8(s)[:, pad] == 0xA5).all()
 
 
 def _rand_mx(rng, rows, K, fmt, lo=112, hi=142):
