@@ -42,6 +42,27 @@ def test_blockwise_bit_exact(shape, block_rows, dtype):
         assert np.array_equal(f32(si).view(np.uint32), wsi.view(np.uint32))
 
 
+def test_blockwise_rowtiles_beyond_one_pass_of_the_grid():
+    """8200 x 16384 bf16 in 1 x 128 tiles: 1,049,600 tiles against the capped
+    grid's 262,144 sixteen-lane groups (16384 workgroups x 16), so every group
+    takes several tiles and the rows past 8192 come from a fifth pass:
+    sampled rows from the first and the last passes bit for bit, codes and
+    scales."""
+    rows, cols = 8200, 16384
+    rng = np.random.default_rng(8200)
+    x32 = (rng.standard_normal((rows, cols), dtype=np.float32)
+           * np.float32(10.0) ** rng.uniform(-3, 3, size=(rows, 1)).astype(np.float32))
+    h = HostTensor(bf16_bits_from_f32(x32), "bf16")
+    del x32
+    announce(f"blockwise rowtiles {rows}x{cols} bf16, sampled rows")
+    q, si = gpu_blockwise(to_device(h), 1, "e4m3")
+    torch.cuda.synchronize()
+    sample = np.unique(np.concatenate([[0, 8191, 8192, 8199], rng.choice(rows, 12, replace=False)]))
+    wq, wsi = scaling.quantize_blockwise(scaling.widen(h.data[sample], "bf16"), 1, 128, "e4m3")
+    assert np.array_equal(u8(q)[sample], wq)
+    assert np.array_equal(f32(si).reshape(rows, -1)[sample].view(np.uint32), wsi.view(np.uint32))
+
+
 def test_blockwise_rejects_columns_not_multiple_of_16():
     x = torch.zeros((5, 300), dtype=torch.float32, device=device())
     q = torch.empty((5, 300), dtype=torch.uint8, device=x.device)
