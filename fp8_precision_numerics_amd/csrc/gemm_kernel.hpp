@@ -175,12 +175,12 @@ __device__ __forceinline__ void run_main_loop(uint8_t* s0, uint8_t* s1, int nful
   if (nfull > 0) {
     for (int g = 0; g < kDmaGroups; ++g) issue_direct(s0, 0, g);
     wait_loads_and_barrier();
+    load_frags(s0);
   } else {
     stage_ragged(0, 0);
     wait_vmem();
     __syncthreads();
   }
-  load_frags(s0);
   int kt = 0;
   for (; kt + 2 < nfull; kt += 2) {
     step(s1, s0, kt + 1);
@@ -190,20 +190,31 @@ __device__ __forceinline__ void run_main_loop(uint8_t* s0, uint8_t* s1, int nful
     step(s1, s0, kt + 1);
     ++kt;
   }
-  // Last full step (its successor, if any, is the ragged step), then the ragged step.
+  // Last full step (its successor, if any, is the ragged step), then the
+  // ragged step, which reads its own fragments: loaded inside the branch on
+  // ragged_k and merged with the registers of the other path, they made the
+  // FP8-core kernel with MX scales spill at the join.  Each step keeps the
+  // loop body's scheduling hint, or its fragment reads are all hoisted ahead
+  // of its MFMAs.
   if (kt < nfull) {
     uint8_t* cur = (kt & 1) ? s1 : s0;
-    uint8_t* nxt = (kt & 1) ? s0 : s1;
     if (ragged_k) stage_ragged(kt + 1, (kt & 1) ^ 1);
     compute(cur, no_dma);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
     ++kt;
     if (ragged_k) {
       wait_vmem();
       __syncthreads();
-      load_frags(nxt);
     }
   }
-  if (kt < nk) compute((kt & 1) ? s1 : s0, no_dma);
+  if (kt < nk) {
+    uint8_t* cur = (kt & 1) ? s1 : s0;
+    load_frags(cur);
+    compute(cur, no_dma);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+  }
   wait_vmem();  // no load may still be writing the LDS when the epilogue reuses it
 }
 
