@@ -103,12 +103,26 @@ __global__ __launch_bounds__(kThreads) void reduce_partials_kernel(const uint4* 
     }
     if (threadIdx.x == 0 && hs.sinv_used) sinv_old = *hs.scale_inv;
   }
+  // Up to eight partials per thread, all loads issued before any is used:
+  // they were just written by workgroups on every XCD, so each one is a
+  // round trip past the local L2, and a loop that waited for each load in
+  // turn paid those round trips one after another.  Slots past `count` read
+  // as zero, which changes neither the maximum nor the sum.
+  constexpr int kPer = 8;
   uint32_t m = 0u;
   unsigned long long c = 0ull;
-  for (int i = threadIdx.x; i < count; i += kThreads) {
-    const uint4 p = partials[i];
-    m = m > p.x ? m : p.x;
-    c += (unsigned long long)p.z | ((unsigned long long)p.w << 32);
+  for (int base = threadIdx.x; base < count; base += kThreads * kPer) {
+    uint4 p[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = base + u * kThreads;
+      p[u] = i < count ? partials[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      m = m > p[u].x ? m : p[u].x;
+      c += (unsigned long long)p[u].z | ((unsigned long long)p[u].w << 32);
+    }
   }
   m = wave_max_u32(m);
   hm = wave_max_u32(hm);
