@@ -32,7 +32,10 @@ __global__ __launch_bounds__(64) void amax_update_kernel(float* __restrict__ his
   const uint32_t a_bits = f2u(*amax);
   uint32_t m = 0u;
   for (int i = lane; i < len; i += 64) {
-    const uint32_t b = (i == h) ? a_bits : f2u(history[i]);
+    // Every slot is loaded, the one at the head replaced afterwards: a load
+    // made conditional on the head waited for the head's own load first.
+    const uint32_t stored = f2u(history[i]);
+    const uint32_t b = (i == h) ? a_bits : stored;
     const uint32_t mag = b & 0x7FFFFFFFu;  // the amax is a magnitude; keep the rule sign-free
     m = m > mag ? m : mag;
   }
