@@ -12,6 +12,8 @@ namespace {
 
 constexpr int64_t kMaxDim = 0x7FFFFFFF;             // kernels index rows/cols with 32-bit ints
 constexpr int64_t kMaxGemmK = int64_t(1) << 23;     // 256 rows x K bytes of a tile slab in a 32-bit buffer offset
+constexpr int64_t kMaxGroupedK = int64_t(1) << 22;  // 512 rows x K bytes (the grouped kernels' widest slab)
+constexpr int64_t kMaxBufferBytes = 0x7FFFFFFF;     // any offset a buffer load carries in one 32-bit register
 constexpr int64_t kMaxElems = (int64_t)1 << 40;     // sanity bound on any one tensor
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_ok[kMaxDevices];         // 0 unknown, 1 gfx950, -1 not usable
@@ -208,6 +210,9 @@ int fp8_gemm_mx(const uint8_t* A, int fa, const uint8_t* sa, const uint8_t* B, i
   if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N)) return FP8MI_ERR_SHAPE;
   if ((K & 127) != 0) return FP8MI_ERR_ALIGN;
   if (((M + 127) / 128) * ((N + 127) / 128) > kMaxDim) return FP8MI_ERR_SHAPE;
+  // The scale loads address a whole scale matrix with one 32-bit offset.
+  if ((K / 32) * FP8MI_MX_SCALE_LD(M) > kMaxBufferBytes || (K / 32) * FP8MI_MX_SCALE_LD(N) > kMaxBufferBytes)
+    return FP8MI_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8MI_OK;
   if (!A || !sa || !B || !sb || !C) return FP8MI_ERR_NULL;
   if (!aligned16(A) || !aligned16(B) || !aligned16(C) || ((uintptr_t)sa & 3) || ((uintptr_t)sb & 3))
@@ -241,7 +246,7 @@ int fp8_grouped_gemm(const uint8_t* A, const float* sinv_a, const uint8_t* B, co
   if (!dtype_ok(ctype)) return FP8MI_ERR_DTYPE;
   if (!accum_ok(accum)) return FP8MI_ERR_ACCUM;
   if (G < 1 || G > 1024) return FP8MI_ERR_SHAPE;
-  if (total_m < 0 || N < 0 || K <= 0 || total_m > kMaxDim || N > kMaxDim || K > kMaxDim)
+  if (total_m < 0 || N < 0 || K <= 0 || total_m > kMaxDim || N > kMaxDim || K > kMaxGroupedK)
     return FP8MI_ERR_SHAPE;
   if (!dims_ok(total_m, K) || !dims_ok(N, K) || !dims_ok((int64_t)G * N, K) || !dims_ok(total_m, N))
     return FP8MI_ERR_SHAPE;

@@ -14,11 +14,13 @@
 //     the fragments of step t+1.
 //
 // Operand slabs are fetched with buffer loads: one buffer resource per tile
-// covers the rows [tile start, M) (or N) of the operand, so rows past the
-// edge fall outside the resource and never touch memory; they only feed
-// output rows or columns that are not stored.  The per-lane offset is the same
-// for every load of a step (the row group and K offset are scalar), which keeps
-// the address state to a single register.
+// covers the rows [tile start, M) (or N) of the operand.  The hardware range
+// check compares only the per-lane (VGPR) offset with the resource's size; the
+// scalar offset is added after the check.  So each load carries its whole row
+// position in the VGPR offset and only the K offset of the step (which stays
+// inside a row that passed the check) in the scalar one: rows past the edge
+// then fail the check, read as zero without touching memory, and only feed
+// output rows or columns that are not stored.
 #pragma once
 
 #include <type_traits>
@@ -95,8 +97,10 @@ constexpr int kDmaGroups = 4;
 // fills position i & 7 of row i >> 3 of that group with the granule stored
 // there under the swizzle (which depends on the row's low 4 bits only, i.e. not
 // on q since NW is even).  One buffer resource per operand covers its rows
-// from the tile start to the edge, so rows past the edge read as zero without
-// touching memory.
+// from the tile start to the edge.  The lane's row offset of load q,
+// voff + q*NW*8*K, is a VGPR operand, so the range check sees the row: rows
+// past the edge read as zero without touching memory.  Only k0 (< K, and the
+// 16 bytes at k0 + granule stay inside the row) is a scalar offset.
 template <int BM, int BN, int NW>
 struct SlabLoader {
   static constexpr int LQA = BM / 8 / NW, LQB = BN / 8 / NW;  // direct-load instructions per wave per step
@@ -128,8 +132,8 @@ struct SlabLoader {
     for (int e = 0; e < PER; ++e) {
       const int d = g * PER + e;
       if (d >= LQA + LQB) break;
-      if (d < LQA) dma_lds16(ra, la + d * NW * 1024, voff, d * NW * 8 * K + k0);
-      else dma_lds16(rb, lb + (d - LQA) * NW * 1024, voff, (d - LQA) * NW * 8 * K + k0);
+      if (d < LQA) dma_lds16(ra, la + d * NW * 1024, voff + d * NW * 8 * K, k0);
+      else dma_lds16(rb, lb + (d - LQA) * NW * 1024, voff + (d - LQA) * NW * 8 * K, k0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -322,7 +326,11 @@ __device__ __forceinline__ void publish_requant_stats(uint32_t amax_bits_lane, u
 // to LDS per wave.  In the stage's scale area the byte of A row r, block b
 // sits at b * BM + mx_scale_pos(r), that of B row r at 4 BM + b * BN +
 // mx_scale_pos(r) (tile starts are multiples of 64).  Rows past the edge only
-// feed outputs that are not stored; bytes past the matrix read as zero.
+// feed outputs that are not stored.  The step's block offset kt * 4 * ld is
+// part of the VGPR offset, so the range check covers the whole address: in an
+// edge tile the positions past ld belong to the next block's rows (in bounds,
+// feeding only outputs that are not stored), and past the last block they read
+// as zero without touching memory.
 __host__ __device__ constexpr int64_t mx_scale_ld(int64_t rows) { return (rows + 63) / 64 * 64; }
 __host__ __device__ constexpr int64_t mx_scale_pos(int64_t r) { return (r & ~int64_t(63)) | ((r & 15) << 2) | ((r >> 4) & 3); }
 
@@ -349,7 +357,7 @@ struct MxScaleLoader {
     }
   }
   __device__ __forceinline__ void issue(uint8_t* scale_area, int kt) const {
-    dma_lds4(r, lds_addr(scale_area) + w * 256, voff, kt * step);
+    dma_lds4(r, lds_addr(scale_area) + w * 256, voff + kt * step, 0);
   }
 };
 

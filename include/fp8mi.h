@@ -304,7 +304,8 @@ FP8MI_API int fp8_quantize_mx(const void* x, int xtype, int64_t rows, int64_t co
  *         here is the instruction's.  The pad bytes only feed outputs that are
  *         not stored.
  * C       device, [M x N] fp32 or bf16, 16-B aligned.
- * K must be a multiple of 128, K <= 2^23.
+ * K must be a multiple of 128, K <= 2^23, and each scale matrix must hold
+ * fewer than 2^31 bytes (else FP8MI_ERR_SHAPE).
  */
 FP8MI_API int fp8_gemm_mx(const uint8_t* A, int fa, const uint8_t* sa, const uint8_t* B, int fb, const uint8_t* sb,
                 int64_t M, int64_t N, int64_t K, void* C, int ctype, void* stream);
@@ -346,7 +347,7 @@ FP8MI_API int fp8_quantize_blockwise(const void* x, int xtype, int64_t rows, int
  *            interval are left untouched.
  * C          device, [total_m x N] of ctype.
  * accum      fp8mi_accum, as for fp8_gemm (applies to each 128-deep partial P).
- * K must be a multiple of 16; G in [1, 1024]; all pointers 16-B aligned.
+ * K must be a multiple of 16, K <= 2^22; G in [1, 1024]; all pointers 16-B aligned.
  */
 FP8MI_API int fp8_grouped_gemm(const uint8_t* A, const float* sinv_a, const uint8_t* B, const float* sinv_b,
                      const int32_t* m_offsets, int32_t G, int64_t total_m, int64_t N, int64_t K,

@@ -116,6 +116,8 @@ def test_mx_argument_errors(lib):
     assert gm(A16, 0, None, A16, 0, A16, 16, 16, 128, A16, 0, None) == ENULL
     assert gm(A16, 0, ctypes.c_void_p(0x10002), A16, 0, A16, 16, 16, 128, A16, 0, None) == EALIGN
     assert gm(A16, 0, A16, A16, 0, A16, 16, 16, 1 << 24, A16, 0, None) == ESHAPE
+    # the A scale matrix (K/32 x 2^20 bytes = 4 GiB) would not fit a 32-bit load offset
+    assert gm(A16, 0, A16, A16, 0, A16, 1 << 20, 16, 1 << 17, A16, 0, None) == ESHAPE
 
 
 def test_quantize_update_argument_errors(lib):
@@ -170,6 +172,7 @@ def test_blockwise_and_grouped_argument_errors(lib):
     assert gg(A16, A16, A16, A16, None, 2, 16, 16, 128, A16, 0, 0, None) == ENULL
     assert gg(A16, A16, A16, A16, A16, 2, 16, 16, 128, A16, 9, 0, None) == EDTYPE
     assert gg(A16, A16, A16, A16, A16, 2, 16, 16, 128, A16, 0, 2, None) == EACCUM
+    assert gg(A16, A16, A16, A16, A16, 2, 16, 16, (1 << 22) + 16, A16, 0, 0, None) == ESHAPE   # K limit
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device path")

@@ -44,7 +44,10 @@ def _run_both(qa, fa, qbT, fb, sa, sb, out_fmt, s_out, accum):
     return (u8(cq), f32(amax)[0], int(sat.item())), (u8(q2), f32(amax2)[0], int(sat2.item()))
 
 
-SHAPES = [(64, 64, 128), (1, 1, 16), (300, 260, 272), (257, 513, 144), (1100, 1030, 384), (1024, 1040, 256)]
+# (1100, 1030, 400) and (1024, 1040, 144): the 256x256-tile path with edge
+# tiles and a ragged last K step.
+SHAPES = [(64, 64, 128), (1, 1, 16), (300, 260, 272), (257, 513, 144), (1100, 1030, 384), (1024, 1040, 256),
+          (1100, 1030, 400), (1024, 1040, 144)]
 
 
 @pytest.mark.parametrize("accum", ["exact", "mfma_fp8"])

@@ -1,0 +1,135 @@
+"""Host-only replay of the GEMM kernels' buffer-load address arithmetic.
+
+The operand slabs and the MXFP8 block scales are fetched with buffer loads
+(fp8_precision_numerics_amd/csrc/gemm_kernel.hpp, SlabLoader and
+MxScaleLoader).  The hardware range check compares the per-lane VGPR offset
+(plus the instruction offset, 0 here) with the resource's byte count; the
+scalar offset is added afterwards and is not checked.  A load whose VGPR
+offset passes the check therefore touches [base + voff + soff, +size): this
+test replays the kernels' offsets for edge tiles of every tile shape the
+dispatch uses and asserts that each such access lies inside the operand, and
+that every tile row inside the operand is actually fetched (so the fix did not
+turn valid rows into zeros)."""
+
+import itertools
+
+import pytest
+
+KBK = 128            # K bytes per main-loop step
+U32_MAX = 0xFFFFFFFF
+
+
+def lds_swz(row):
+    return (row & 6) | ((row >> 3) & 1)
+
+
+def slab_accesses(BM, BN, NW, rows_left_a, rows_left_b, K, kt):
+    """(operand, tile_row, byte_start, size, checked_offset, num_records) of every
+    direct-to-LDS load of step kt, as SlabLoader::issue forms them."""
+    LQA, LQB = BM // 8 // NW, BN // 8 // NW
+    out = []
+    k0 = kt * KBK
+    for w in range(NW):
+        for lane in range(64):
+            lrow = w * 8 + (lane >> 3)
+            voff = lrow * K + (((lane & 7) ^ lds_swz(lrow)) & 7) * 16
+            for d in range(LQA + LQB):
+                if d < LQA:
+                    op, q, rows_left = "A", d, rows_left_a
+                else:
+                    op, q, rows_left = "B", d - LQA, rows_left_b
+                v = voff + q * NW * 8 * K          # VGPR operand
+                s = k0                             # scalar operand
+                assert v < 2 ** 31, "the VGPR offset must fit a signed 32-bit register"
+                nrec = min(rows_left * K, U32_MAX)
+                out.append((op, lrow + q * NW * 8, v + s, 16, v, nrec))
+    return out
+
+
+# (BM, BN, NW): dense exact 256x256 / 4 waves; dense FP8 and MX 256x256 / 8
+# waves; small problems 128x128 / 4 waves; grouped FP8 128x512 / 8 waves;
+# grouped exact 128x128 / 4 waves.
+SHAPES = [(256, 256, 4), (256, 256, 8), (128, 128, 4), (128, 512, 8)]
+
+
+@pytest.mark.parametrize("BM,BN,NW", SHAPES)
+@pytest.mark.parametrize("K", [128, 400, 4096])
+def test_slab_loads_stay_inside_the_operand(BM, BN, NW, K):
+    nfull = K // KBK
+    for rows_a, rows_b in [(1, BN), (BM, 1), (BM - 1, BN - 7), (9, 17), (BM // 2 + 3, BN // 2 - 5),
+                           (BM, BN), (8 * NW - 1, 8 * NW + 1)]:
+        for kt in sorted({0, nfull - 1}):
+            fetched = {"A": set(), "B": set()}
+            for op, row, start, size, chk, nrec in slab_accesses(BM, BN, NW, rows_a, rows_b, K, kt):
+                rows_left = rows_a if op == "A" else rows_b
+                if chk + size > nrec:           # fails the range check: reads zero, touches nothing
+                    assert row >= rows_left, (op, row, rows_left)
+                    continue
+                assert row < rows_left, (op, row, rows_left)
+                assert 0 <= start and start + size <= rows_left * K, (op, row, start, rows_left * K)
+                # the access stays inside its own row and inside the step's K slice
+                assert start // K == row and kt * KBK <= start % K and start % K + size <= (kt + 1) * KBK
+                fetched[op].add((row, start % K))
+            for op, rows_left in (("A", rows_a), ("B", rows_b)):
+                want = {(r, kt * KBK + g * 16) for r in range(min(rows_left, BM if op == "A" else BN))
+                        for g in range(8)}
+                assert fetched[op] == want, op
+
+
+def test_old_scalar_row_offset_would_have_left_the_operand():
+    """The form the loads had before (row group in the unchecked scalar offset)
+    reads past the end of an exactly sized operand in an edge tile; kept as a
+    record of why the offset moved."""
+    BM, NW, K, rows_left = 256, 4, 256, 40
+    bad = 0
+    for w, lane, d in itertools.product(range(NW), range(64), range(BM // 8 // NW)):
+        lrow = w * 8 + (lane >> 3)
+        voff = lrow * K + (((lane & 7) ^ lds_swz(lrow)) & 7) * 16
+        soff = d * NW * 8 * K
+        if voff + 16 <= rows_left * K and voff + soff + 16 > rows_left * K:
+            bad += 1
+    assert bad > 0
+
+
+def mx_scale_ld(rows):
+    return (rows + 63) // 64 * 64
+
+
+def mx_scale_pos(r):
+    return (r & ~63) | ((r & 15) << 2) | ((r >> 4) & 3)
+
+
+@pytest.mark.parametrize("M,N,K", [(320, 300, 256), (64, 1000, 128), (1100, 1030, 512), (256, 256, 384)])
+def test_mx_scale_loads_stay_inside_the_scale_matrices(M, N, K):
+    """MxScaleLoader (256x256 tiles, 8 waves): one dword per lane per step, the
+    step's block offset in the VGPR operand.  Every dword that passes the check
+    lies inside its scale matrix, and every (row < M, block) byte a tile needs is
+    among the bytes fetched."""
+    BM = BN = 256
+    NW = 8
+    tiles_m, tiles_n = -(-M // BM), -(-N // BN)
+    ld_a, ld_b = mx_scale_ld(M), mx_scale_ld(N)
+    for tm, tn in itertools.product(range(tiles_m), range(tiles_n)):
+        m0, n0 = tm * BM, tn * BN
+        for kt in range(K // 128):
+            got_a, got_b = set(), set()
+            for w, lane in itertools.product(range(NW), range(64)):
+                e = w * 64 + lane
+                if w < BM // 64:
+                    ld, base_row, idx, rows, got = ld_a, m0, e, M, got_a
+                    area = BM
+                else:
+                    ld, base_row, idx, rows, got = ld_b, n0, e - BM, N, got_b
+                    area = BN
+                voff = (idx // (area // 4)) * ld + base_row + 4 * (idx % (area // 4)) + kt * 4 * ld
+                nrec = (K // 32) * ld
+                assert voff < 2 ** 31
+                if voff + 4 > nrec:
+                    continue
+                assert voff + 4 <= nrec
+                for b in range(4):
+                    got.add(voff + b)
+            for rows, ld, r0, got in ((M, ld_a, m0, got_a), (N, ld_b, n0, got_b)):
+                for r in range(r0, min(rows, r0 + BM)):
+                    for blk in range(4 * kt, 4 * kt + 4):
+                        assert blk * ld + mx_scale_pos(r) in got, (r, blk)

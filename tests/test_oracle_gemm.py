@@ -175,3 +175,64 @@ def test_requant_bracket_hand_values():
     # a bracket across zero: the amax bracket starts at 0, negative and positive codes both admitted
     r = gemm.requant_bracket(np.array([0.25]), np.array([0.5]), np.float32(1.0), "e4m3")
     assert r["lo"][0] == -0.25 and r["hi"][0] == 0.75 and r["amax"] == (0.0, 0.75)
+
+
+def _fraction_grouped_bound(qa, sa, qb, sb, offs, fa="e4m3", fb="e4m3", block=128):
+    """1e-5 * sum_kb |sa[m,kb]| |sb[g,n/128,kb]| sum_{k in kb} |a_k| |b_k|, exactly, by loops."""
+    G, N, K = qb.shape
+    A = np.abs(codec.decode(qa, fa))
+    out = np.zeros((int(offs[-1]), N))
+    for g in range(G):
+        B = np.abs(codec.decode(qb[g], fb))
+        for m in range(int(offs[g]), int(offs[g + 1])):
+            for n in range(N):
+                tot = Fraction(0)
+                for k in range(K):
+                    tot += Fraction(float(A[m, k])) * Fraction(float(B[n, k])) \
+                        * abs(Fraction(float(sa[m, k // block]))) * abs(Fraction(float(sb[g, n // block, k // block])))
+                out[m, n] = float(Fraction(1, 100000) * tot)
+    return out
+
+
+def test_grouped_abs_bound_against_fraction_brute_force():
+    """The grouped tolerance, element by element, against an exact evaluation of
+    its definition: an empty expert, N and K not multiples of 128 (partial
+    weight and K blocks), block scales that differ per row, per 128-column
+    block and per K block, some of them negative (the bound takes magnitudes).
+    A wrong block index, a missing |.| or a dropped K block changes elements."""
+    rng = np.random.default_rng(11)
+    offs = np.array([0, 3, 3, 7])                  # expert 1 is empty
+    K, N, G = 300, 150, 3                          # 3 K blocks (last 44 deep), 2 N blocks (last 22 wide)
+    qa = _rand_codes(rng, (7, K), "e4m3")
+    qb = _rand_codes(rng, (G, N, K), "e4m3")
+    sa = (rng.uniform(0.5, 2, size=(7, 3)) * 2.0 ** rng.integers(-6, 6, size=(7, 3))).astype(np.float32)
+    sb = (rng.uniform(0.5, 2, size=(G, 2, 3)) * 2.0 ** rng.integers(-6, 6, size=(G, 2, 3))).astype(np.float32)
+    sa[1, 2] *= -1
+    sb[2, 1, 0] *= -1
+    got = gemm.grouped_abs_bound(qa, sa, qb, sb, offs)
+    want = _fraction_grouped_bound(qa, sa, qb, sb, offs)
+    assert np.allclose(got, want, rtol=1e-12, atol=0)
+    # a row subset gives the same rows
+    rows = np.array([6, 0, 3])
+    assert np.array_equal(gemm.grouped_abs_bound(qa, sa, qb, sb, offs, rows=rows), got[rows])
+    # and the bound really is the tolerance of the grouped sum: the exact grouped
+    # sum with every term's sign dropped is 1e5 times the bound
+    mag = gemm.grouped_gemm(np.where(qa == 0x80, 0, qa & 0x7F).astype(np.uint8), np.abs(sa),
+                            (qb & 0x7F).astype(np.uint8), np.abs(sb), offs)
+    assert np.allclose(mag * 1e-5, got, rtol=1e-12, atol=0)
+
+
+def test_grouped_abs_bound_mixed_formats_and_single_block():
+    """E5M2 weights against E4M3 activations; K = 16 (one partial block) and
+    N = 1: the bound reduces to 1e-5 |sa| |sb| sum_k |a_k b_k|."""
+    rng = np.random.default_rng(12)
+    qa = _rand_codes(rng, (2, 16), "e4m3")
+    qb = _rand_codes(rng, (1, 1, 16), "e5m2")
+    sa = np.array([[0.5], [-3.0]], dtype=np.float32)
+    sb = np.array([[[0.125]]], dtype=np.float32)
+    got = gemm.grouped_abs_bound(qa, sa, qb, sb, np.array([0, 2]), fa="e4m3", fb="e5m2")
+    A, B = np.abs(codec.decode(qa, "e4m3")), np.abs(codec.decode(qb[0, 0], "e5m2"))
+    for m, s in ((0, 0.5), (1, 3.0)):
+        want = Fraction(1, 100000) * Fraction(s) * Fraction(0.125) * sum(
+            (Fraction(float(x)) * Fraction(float(y)) for x, y in zip(A[m], B)), Fraction(0))
+        assert abs(got[m, 0] - float(want)) <= 1e-12 * float(want)
