@@ -19,7 +19,7 @@ __all__ = ["E4M3", "E5M2", "F32", "BF16", "ACCUM_EXACT", "ACCUM_MFMA_FP8", "QUAN
            "status_string", "version", "fp8_quantize", "fp8_amax_update", "fp8_gemm",
            "fp8_quantize_blockwise", "fp8_grouped_gemm", "fp8_gemm_requant", "fp8_shared_scale", "fp8_dequant_sum",
            "fp8_quantize_mx", "fp8_gemm_mx", "mx_scale_ld", "mx_scale_pos", "fp8_quantize_update",
-           "EXPORTED_SYMBOLS"]
+           "fp8_quantize_update_noalloc", "EXPORTED_SYMBOLS"]
 
 E4M3, E5M2 = 0, 1
 F32, BF16 = 0, 1
@@ -31,7 +31,7 @@ ACCUMS = {"exact": ACCUM_EXACT, "mfma_fp8": ACCUM_MFMA_FP8, ACCUM_EXACT: ACCUM_E
 EXPORTED_SYMBOLS = ("fp8mi_status_string", "fp8mi_version", "fp8_quantize", "fp8_amax_update",
                     "fp8_gemm", "fp8_quantize_blockwise", "fp8_grouped_gemm", "fp8_gemm_requant",
                     "fp8_shared_scale", "fp8_dequant_sum", "fp8_quantize_mx", "fp8_gemm_mx",
-                    "fp8_quantize_update")
+                    "fp8_quantize_update", "fp8_quantize_update_noalloc")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -74,6 +74,9 @@ def load_library():
     lib.fp8_quantize_update.argtypes = [vp, ctypes.c_int, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                         vp, i32, vp, vp, vp, vp, vp, vp]
     lib.fp8_quantize_update.restype = ctypes.c_int
+    lib.fp8_quantize_update_noalloc.argtypes = [vp, ctypes.c_int, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, i32,
+                                                vp, vp, vp, vp, vp, vp]
+    lib.fp8_quantize_update_noalloc.restype = ctypes.c_int
     lib.fp8_amax_update.argtypes = [vp, i32, vp, vp, ctypes.c_int, vp, vp, vp, vp]
     lib.fp8_amax_update.restype = ctypes.c_int
     lib.fp8_gemm.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, ctypes.c_int,
@@ -224,6 +227,31 @@ def fp8_quantize_update(x, fmt, history, head, scale, scale_inv, amax, q=None, q
             _p(x), xtype, rows, cols, _fmt(fmt), _p(q), _p(q_t), _p(amax), _p(sat), _p(workspace),
             workspace.numel() if workspace is not None else 0, _p(history), history.numel(), _p(head), _p(scale),
             _p(scale_inv), _p(status), _p(scale_inv_used), _stream(stream)))
+
+
+def fp8_quantize_update_noalloc(x, fmt, history, head, scale, scale_inv, amax, q=None, q_t=None, sat=None,
+                                status=None, scale_inv_used=None, stream=None) -> None:
+    """fp8_quantize_update with the library's own per-GPU scratch instead of a workspace: allocates nothing.
+    Calls that may overlap on one GPU must not be issued (they share the scratch)."""
+    lib = load_library()
+    dev = x.device
+    _check(x, "x", (torch.float32, torch.bfloat16), None, dev)
+    rows, cols = _rows_cols(x)
+    _check(q, "q", torch.uint8, rows * cols, dev)
+    _check(q_t, "q_t", torch.uint8, rows * cols, dev)
+    _check(history, "history", torch.float32, None, dev)
+    _check(head, "head", torch.int32, 1, dev)
+    _check(scale, "scale", torch.float32, 1, dev)
+    _check(scale_inv, "scale_inv", torch.float32, 1, dev)
+    _check(amax, "amax", torch.float32, 1, dev)
+    _check(sat, "sat", torch.int64, 1, dev)
+    _check(status, "status", torch.int32, 1, dev)
+    _check(scale_inv_used, "scale_inv_used", torch.float32, 1, dev)
+    xtype = F32 if x.dtype == torch.float32 else BF16
+    with torch.cuda.device(dev):
+        _call("fp8_quantize_update_noalloc", lib.fp8_quantize_update_noalloc(
+            _p(x), xtype, rows, cols, _fmt(fmt), _p(q), _p(q_t), _p(amax), _p(sat), _p(history), history.numel(),
+            _p(head), _p(scale), _p(scale_inv), _p(status), _p(scale_inv_used), _stream(stream)))
 
 
 def fp8_amax_update(history, head, amax, fmt, scale, scale_inv, status=None, stream=None) -> None:

@@ -35,6 +35,14 @@ int check_device() {
       if (a[0] == 'g' && a[1] == 'f' && a[2] == 'x' && a[3] == '9' && a[4] == '5' && a[5] == '0')
         state = 1;
     }
+    // Set-up on the first call that sees this device: the device address of
+    // the library-owned scratch (fp8_quantize_update_noalloc), looked up while
+    // the device is current.  A failure here is reported by that entry point,
+    // which retries the lookup, and does not affect the others.
+    if (state == 1) {
+      void* scratch = nullptr;
+      (void)fp8mi::noalloc_scratch(&scratch);
+    }
     g_device_ok[dev].store(state, std::memory_order_relaxed);
   }
   return state == 1 ? FP8MI_OK : FP8MI_ERR_DEVICE;
@@ -112,6 +120,30 @@ int fp8_quantize_update(const void* x, int xtype, int64_t rows, int64_t cols, in
   const fp8mi::HistoryArgs hs{history, history_len, head, scale, scale_inv, status, fmt, scale_inv_used};
   return launched(fp8mi::launch_quantize(x, xtype, rows, cols, fmt, scale, q, q_t, amax, sat, workspace,
                                          workspace_bytes, (hipStream_t)stream, hs));
+}
+
+int fp8_quantize_update_noalloc(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, uint8_t* q,
+                                uint8_t* q_t, float* amax, unsigned long long* sat, float* history,
+                                int32_t history_len, int32_t* head, float* scale, float* scale_inv, int32_t* status,
+                                float* scale_inv_used, void* stream) {
+  if (!dtype_ok(xtype)) return FP8MI_ERR_DTYPE;
+  if (!fmt_ok(fmt)) return FP8MI_ERR_FORMAT;
+  if (!dims_ok(rows, cols)) return FP8MI_ERR_SHAPE;
+  if (history_len < 1 || history_len > 4096) return FP8MI_ERR_SHAPE;
+  const int64_t n = rows * cols;
+  if (!amax || !history || !head || !scale || !scale_inv) return FP8MI_ERR_NULL;
+  if (n > 0 && !x) return FP8MI_ERR_NULL;
+  if ((x && !aligned16(x)) || (q && !aligned16(q)) || (q_t && !aligned16(q_t))) return FP8MI_ERR_ALIGN;
+  if (q_t && ((rows & 15) || (cols & 15))) return FP8MI_ERR_ALIGN;
+  if (q_t && (rows + 127) / 128 > 65535) return FP8MI_ERR_SHAPE;
+  if ((cols + 127) / 128 > kMaxDim) return FP8MI_ERR_SHAPE;
+  const int dev = check_device();
+  if (dev != FP8MI_OK) return dev;
+  const fp8mi::HistoryArgs hs{history, history_len, head, scale, scale_inv, status, fmt, scale_inv_used};
+  const hipError_t e = fp8mi::launch_quantize_noalloc(x, xtype, rows, cols, fmt, q, q_t, amax, sat,
+                                                      (hipStream_t)stream, hs);
+  if (e == hipErrorInvalidSymbol || e == hipErrorInvalidDevice) return FP8MI_ERR_DEVICE;
+  return launched(e);
 }
 
 int fp8_amax_update(float* history, int32_t history_len, int32_t* head, const float* amax, int fmt,

@@ -27,6 +27,21 @@ hipError_t launch_quantize(const void* x, int xtype, int64_t rows, int64_t cols,
                            hipStream_t stream, HistoryArgs hs = HistoryArgs{nullptr, 0, nullptr, nullptr, nullptr,
                                                                            nullptr, 0, nullptr});
 
+// Bytes of the library-owned scratch behind fp8_quantize_update_noalloc
+// (FP8MI_NOALLOC_SCRATCH_BYTES): 4096 partial slots of 16 bytes, more than any
+// cast grid uses (a grid is capped at the slots it is given).
+constexpr size_t kNoallocScratchBytes = 65536;
+
+// The device address of that scratch on the current device, looked up once
+// per device (hipGetSymbolAddress) and cached; the library's set-up calls it
+// when it first sees a device.
+hipError_t noalloc_scratch(void** out);
+
+// launch_quantize with the library-owned scratch as the workspace.
+hipError_t launch_quantize_noalloc(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, uint8_t* q,
+                                   uint8_t* q_t, float* amax, unsigned long long* sat, hipStream_t stream,
+                                   HistoryArgs hs);
+
 hipError_t launch_quantize_blockwise(const void* x, int xtype, int64_t rows, int64_t cols,
                                      int block_rows, int fmt, uint8_t* q, float* scale_inv,
                                      hipStream_t stream);

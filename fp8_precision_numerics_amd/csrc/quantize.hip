@@ -19,6 +19,9 @@
 // across the wavefront with shuffles, across the workgroup in LDS, and across
 // workgroups through per-workgroup partials (or one atomicMax per workgroup
 // without a workspace); the saturation count is a wave ballot + popcount.
+#include <atomic>
+#include <mutex>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -737,6 +740,55 @@ hipError_t launch_quantize(const void* x, int xtype, int64_t rows, int64_t cols,
     return launch_amax_update(hs.history, hs.len, hs.head, amax, hs.fmt, hs.scale, hs.scale_inv, hs.status, stream);
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The library's own scratch for callers that cannot allocate
+// (fp8_quantize_update_noalloc): the per-workgroup partials of one cast, in a
+// file-scope device array instead of a caller workspace.  Each GPU holds its
+// own copy until the process ends.  Host code never uses the array's name as
+// an address (on the host it names a stand-in, not device memory): the device
+// address is looked up once per device with hipGetSymbolAddress, with that
+// device current, and kept in g_scratch_ptr.  Every workgroup of a cast writes
+// its own slot and the reduction reads only the slots of that grid, so the
+// contents a previous call left behind never need clearing.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t noalloc_scratch(void** out) {
+  *out = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+hipError_t launch_quantize_noalloc(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, uint8_t* q,
+                                   uint8_t* q_t, float* amax, unsigned long long* sat, hipStream_t stream,
+                                   HistoryArgs hs) {
+  void* ws = nullptr;
+  const hipError_t e = noalloc_scratch(&ws);
+  if (e != hipSuccess) return e;
+  return launch_quantize(x, xtype, rows, cols, fmt, hs.scale, q, q_t, amax, sat, ws, kNoallocScratchBytes, stream,
+                         hs);
 }
 
 hipError_t launch_quantize_blockwise(const void* x, int xtype, int64_t rows, int64_t cols,

@@ -176,6 +176,35 @@ FP8MI_API int fp8_quantize_update(const void* x, int xtype, int64_t rows, int64_
                         int32_t* status, float* scale_inv_used, void* stream);
 
 /*
+ * fp8_quantize_update_noalloc — fp8_quantize_update for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the per-workgroup partials go to a scratch
+ * array the library holds on each GPU (FP8MI_NOALLOC_SCRATCH_BYTES, in the
+ * library's device data, kept until the process ends) instead of a caller
+ * workspace.  The call allocates nothing and frees nothing.
+ *
+ * Arguments, results and errors are those of fp8_quantize_update without
+ * workspace / workspace_bytes; the outputs are bit for bit the same as
+ * fp8_quantize_update with a workspace of FP8MI_QUANTIZE_WORKSPACE_BYTES.
+ * The scratch holds 4096 partial slots, more than any cast grid uses, so no
+ * tensor size is refused for want of scratch (sizes are limited as for
+ * fp8_quantize_update).  FP8MI_ERR_DEVICE if the scratch's device address
+ * cannot be found on the current device.
+ *
+ * All calls on one GPU share its scratch: two calls that may run at the same
+ * time on one GPU (different streams without ordering between them) race on
+ * it and must not be issued.  Calls ordered on one stream, or on streams that
+ * are synchronised with each other, are safe; what a previous call left in the
+ * scratch never affects the next one.
+ */
+#define FP8MI_NOALLOC_SCRATCH_BYTES 65536
+
+FP8MI_API int fp8_quantize_update_noalloc(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, uint8_t* q,
+                                uint8_t* q_t, float* amax, unsigned long long* sat, float* history,
+                                int32_t history_len, int32_t* head, float* scale, float* scale_inv, int32_t* status,
+                                float* scale_inv_used, void* stream);
+
+/*
  * fp8_gemm — FP8 x FP8 GEMM with FP32 accumulation and the x(1/scale) restore
  * in the epilogue ([TE] §4.2.4; [FMT] "Technical insight").
  *
