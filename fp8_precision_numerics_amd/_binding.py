@@ -79,8 +79,8 @@ def load_library():
     lib.fp8_quantize_update_noalloc.restype = ctypes.c_int
     lib.fp8_amax_update.argtypes = [vp, i32, vp, vp, ctypes.c_int, vp, vp, vp, vp]
     lib.fp8_amax_update.restype = ctypes.c_int
-    lib.fp8_gemm.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, ctypes.c_int,
-                             ctypes.c_int, vp]
+    lib.fp8_gemm.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, vp, vp,
+                             ctypes.c_int, ctypes.c_int, vp]
     lib.fp8_gemm.restype = ctypes.c_int
     lib.fp8_quantize_blockwise.argtypes = [vp, ctypes.c_int, i64, i64, i32, ctypes.c_int, vp, vp, vp]
     lib.fp8_quantize_blockwise.restype = ctypes.c_int
@@ -270,8 +270,9 @@ def fp8_amax_update(history, head, amax, fmt, scale, scale_inv, status=None, str
                                                      _stream(stream)))
 
 
-def fp8_gemm(a, fa, b, fb, sinv_a, sinv_b, c, accum="exact", stream=None) -> None:
-    """C[M x N] = (A[M x K] · B[N x K]ᵀ) · sinv_a · sinv_b with FP8 codes A, B.
+def fp8_gemm(a, fa, b, fb, sinv_a, sinv_b, c, accum="exact", b_trans=False, stream=None) -> None:
+    """C[M x N] = (A[M x K] · B_kn) · sinv_a · sinv_b with FP8 codes A, B, where
+    B_kn = b.T for b [N x K] (b_trans False) or b itself for b [K x N] (b_trans True).
 
     accum: "exact" (every product exact, fp32 sums) or "mfma_fp8" (native FP8
     matrix cores; see include/fp8mi.h for their arithmetic).
@@ -284,13 +285,14 @@ def fp8_gemm(a, fa, b, fb, sinv_a, sinv_b, c, accum="exact", stream=None) -> Non
     _check(sinv_b, "sinv_b", torch.float32, 1, dev)
     _check(c, "c", (torch.float32, torch.bfloat16), None, dev)
     M, K = a.shape
-    N, K2 = b.shape
+    K2, N = b.shape if b_trans else (b.shape[1], b.shape[0])
     if K2 != K or tuple(c.shape) != (M, N):
-        raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)}, c {tuple(c.shape)}")
+        raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)} (b_trans={bool(b_trans)}), "
+                         f"c {tuple(c.shape)}")
     ctype = F32 if c.dtype == torch.float32 else BF16
     with torch.cuda.device(dev):
-        _call("fp8_gemm", lib.fp8_gemm(_p(a), _fmt(fa), _p(b), _fmt(fb), M, N, K, _p(sinv_a), _p(sinv_b),
-                                       _p(c), ctype, _accum(accum), _stream(stream)))
+        _call("fp8_gemm", lib.fp8_gemm(_p(a), _fmt(fa), _p(b), _fmt(fb), 1 if b_trans else 0, M, N, K, _p(sinv_a),
+                                       _p(sinv_b), _p(c), ctype, _accum(accum), _stream(stream)))
 
 
 def fp8_gemm_requant(a, fa, b, fb, sinv_a, sinv_b, out_fmt, out_scale, cq, amax=None, sat=None, accum="exact",

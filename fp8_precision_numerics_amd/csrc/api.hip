@@ -75,7 +75,7 @@ const char* fp8mi_status_string(int status) {
   }
 }
 
-int fp8mi_version(void) { return 700; }
+int fp8mi_version(void) { return 800; }
 
 int fp8_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt, const float* scale,
                  uint8_t* q, uint8_t* q_t, float* amax, unsigned long long* sat, void* workspace,
@@ -157,7 +157,7 @@ int fp8_amax_update(float* history, int32_t history_len, int32_t* head, const fl
                                             status, (hipStream_t)stream));
 }
 
-int fp8_gemm(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t M, int64_t N, int64_t K,
+int fp8_gemm(const uint8_t* A, int fa, const uint8_t* B, int fb, int b_trans, int64_t M, int64_t N, int64_t K,
              const float* sinv_a, const float* sinv_b, void* C, int ctype, int accum, void* stream) {
   if (!fmt_ok(fa) || !fmt_ok(fb)) return FP8MI_ERR_FORMAT;
   if (!dtype_ok(ctype)) return FP8MI_ERR_DTYPE;
@@ -165,13 +165,16 @@ int fp8_gemm(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t M, int6
   if (M < 0 || N < 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxGemmK) return FP8MI_ERR_SHAPE;
   if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N)) return FP8MI_ERR_SHAPE;
   if ((K & 15) != 0) return FP8MI_ERR_ALIGN;
+  // [K x N] B: whole 16-byte granules per K row, and every offset into it within 31 bits.
+  if (b_trans && (N & 15) != 0) return FP8MI_ERR_ALIGN;
+  if (b_trans && K * N > kMaxBufferBytes) return FP8MI_ERR_SHAPE;
   if (((M + 127) / 128) * ((N + 127) / 128) > kMaxDim) return FP8MI_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8MI_OK;
   if (!A || !B || !sinv_a || !sinv_b || !C) return FP8MI_ERR_NULL;
   if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return FP8MI_ERR_ALIGN;
   const int dev = check_device();
   if (dev != FP8MI_OK) return dev;
-  return launched(fp8mi::launch_gemm(A, fa, B, fb, M, N, K, sinv_a, sinv_b, C, ctype, accum,
+  return launched(fp8mi::launch_gemm(A, fa, B, fb, b_trans ? 1 : 0, M, N, K, sinv_a, sinv_b, C, ctype, accum,
                                      (hipStream_t)stream));
 }
 

@@ -7,13 +7,13 @@
 
 namespace fp8mi {
 
-template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, int MODE>
+template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, int MODE, bool BT>
 inline hipError_t gemm_run(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sa,
                            const float* sb, void* C, const RequantArgs& rq, hipStream_t st,
                            const MxScales& mxs = MxScales{nullptr, nullptr}) {
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
   const int group_m = 16;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, FA, FB, OUT, MODE>), dim3((unsigned)(tiles_m * tiles_n)),
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, FA, FB, OUT, MODE, BT>), dim3((unsigned)(tiles_m * tiles_n)),
                      dim3(64 * WM * WN), 0, st, A, B, (int)M, (int)N, (int)K, sa, sb, C, tiles_m, tiles_n, group_m,
                      rq, mxs);
   return hipGetLastError();
@@ -22,26 +22,27 @@ inline hipError_t gemm_run(const uint8_t* A, const uint8_t* B, int64_t M, int64_
 // 256x256 tiles.  fp16 path: 4 wavefronts (one per SIMD, 128x128 each, the
 // accumulators in the AGPR half of the register file).  FP8 path: 8
 // wavefronts (two per SIMD, 64x128 each) to hide more latency.  Small
-// problems: 128x128 tiles of four 64x64 wavefronts.
-template <int FA, int FB, int OUT, int MODE>
+// problems: 128x128 tiles of four 64x64 wavefronts.  BT: B stored [K x N]
+// (read through the LDS transpose path), same tiles.
+template <int FA, int FB, int OUT, int MODE, bool BT = false>
 inline hipError_t gemm_dispatch_shape(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K,
                                       const float* sa, const float* sb, void* C, const RequantArgs& rq,
                                       hipStream_t st, const MxScales& mxs = MxScales{nullptr, nullptr}) {
   if (M >= 1024 && N >= 1024) {
-    if constexpr (MODE == kAccumExact) return gemm_run<256, 256, 2, 2, FA, FB, OUT, MODE>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
-    else return gemm_run<256, 256, 4, 2, FA, FB, OUT, MODE>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
+    if constexpr (MODE == kAccumExact) return gemm_run<256, 256, 2, 2, FA, FB, OUT, MODE, BT>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
+    else return gemm_run<256, 256, 4, 2, FA, FB, OUT, MODE, BT>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
   }
-  return gemm_run<128, 128, 2, 2, FA, FB, OUT, MODE>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
+  return gemm_run<128, 128, 2, 2, FA, FB, OUT, MODE, BT>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
 }
 
-template <int OUT, int MODE>
+template <int OUT, int MODE, bool BT = false>
 inline hipError_t gemm_dispatch_fmt(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t M, int64_t N,
                                     int64_t K, const float* sa, const float* sb, void* C, const RequantArgs& rq,
                                     hipStream_t st, const MxScales& mxs = MxScales{nullptr, nullptr}) {
-  if (fa == kE4M3 && fb == kE4M3) return gemm_dispatch_shape<kE4M3, kE4M3, OUT, MODE>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
-  if (fa == kE5M2 && fb == kE4M3) return gemm_dispatch_shape<kE5M2, kE4M3, OUT, MODE>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
-  if (fa == kE4M3 && fb == kE5M2) return gemm_dispatch_shape<kE4M3, kE5M2, OUT, MODE>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
-  return gemm_dispatch_shape<kE5M2, kE5M2, OUT, MODE>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
+  if (fa == kE4M3 && fb == kE4M3) return gemm_dispatch_shape<kE4M3, kE4M3, OUT, MODE, BT>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
+  if (fa == kE5M2 && fb == kE4M3) return gemm_dispatch_shape<kE5M2, kE4M3, OUT, MODE, BT>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
+  if (fa == kE4M3 && fb == kE5M2) return gemm_dispatch_shape<kE4M3, kE5M2, OUT, MODE, BT>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
+  return gemm_dispatch_shape<kE5M2, kE5M2, OUT, MODE, BT>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
 }
 
 }  // namespace fp8mi

@@ -101,25 +101,58 @@ constexpr int kDmaGroups = 4;
 // voff + q*NW*8*K, is a VGPR operand, so the range check sees the row: rows
 // past the edge read as zero without touching memory.  Only k0 (< K, and the
 // 16 bytes at k0 + granule stay inside the row) is a scalar offset.
-template <int BM, int BN, int NW>
+//
+// BT (B stored [K x N], N contiguous, as the operand of C = A B): the B slab of
+// a step is 128 K rows of BN bytes in its natural orientation, the 16-byte
+// granule q of K row r at position q ^ (r & 7) (see bt_lds_offset).  Wave
+// load e fills K rows e*RPB .. +RPB-1 (RPB = 1024 / BN rows per instruction);
+// lane i fills position i % (BN/16) of row i / (BN/16) with the granule that
+// belongs there.  Since NW is even, the parity of e and so the lane's source
+// granule is the same for every load of the wave: one VGPR offset serves them
+// all.  Columns at or past N get an offset above the resource's size, so they
+// read as zero without touching memory; rows at or past K can only occur in a
+// ragged last step, whose loads carry the row in the VGPR offset as well.
+template <int BN>
+__device__ __forceinline__ int bt_lds_offset(int krow, int col) {
+  return krow * BN + ((((col >> 4) ^ (krow & 7)) << 4) | (col & 15));
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;  // above any operand size these loads allow (< 2^31 bytes)
+
+template <int BM, int BN, int NW, bool BT = false>
 struct SlabLoader {
   static constexpr int LQA = BM / 8 / NW, LQB = BN / 8 / NW;  // direct-load instructions per wave per step
   static constexpr int PER = (LQA + LQB + kDmaGroups - 1) / kDmaGroups;
+  static constexpr int RPB = 1024 / BN;                       // BT: K rows per load instruction
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows must split evenly over the wavefronts");
   static_assert(NW % 2 == 0, "the swizzle of a lane's load must not depend on its row group");
+  static_assert(!BT || (BN >= 128 && BN <= 1024 && 128 % (RPB * NW) == 0), "BT slab shape");
   const uint8_t* A;
   const uint8_t* B;
   int64_t m0, m_end, n0, n_end;
   int K, w, voff;
+  int ldb;            // BT: bytes per K row of B (= N)
+  uint32_t voff_bt;   // BT: the lane's offset in the first K row group, or kOutOfRange
   __amdgpu_buffer_rsrc_t ra, rb;
 
   __device__ __forceinline__ SlabLoader(const uint8_t* A_, int64_t m0_, int64_t m_end_, const uint8_t* B_,
                                         int64_t n0_, int64_t n_end_, int K_, int w_, int lane)
       : A(A_), B(B_), m0(m0_), m_end(m_end_), n0(n0_), n_end(n_end_), K(K_), w(w_) {
     ra = operand_rsrc(A + m0 * K, m_end - m0, K);
-    rb = operand_rsrc(B + n0 * K, n_end - n0, K);
     const int lrow = w * 8 + (lane >> 3);
     voff = lrow * K + (((lane & 7) ^ lds_swz(lrow)) & 7) * 16;
+    if constexpr (BT) {
+      ldb = (int)n_end;
+      rb = operand_rsrc(B, K, ldb);  // the whole [K x N] matrix
+      const int r = w * RPB + lane / (BN / 16);                  // K row of load 0 (same parity for every load)
+      const int q = (lane % (BN / 16)) ^ (r & 7);                // source granule of the lane
+      const int64_t col = n0 + 16 * q;
+      voff_bt = col < n_end ? (uint32_t)(r * ldb + col) : kOutOfRange;
+    } else {
+      ldb = K;
+      voff_bt = 0;
+      rb = operand_rsrc(B + n0 * K, n_end - n0, K);
+    }
   }
   // Group g of the loads of step kt into the stage at `dst`: loads
   // d = g*PER .. of the wave's LQA + LQB (A first).  A group is pinned where it
@@ -133,14 +166,25 @@ struct SlabLoader {
       const int d = g * PER + e;
       if (d >= LQA + LQB) break;
       if (d < LQA) dma_lds16(ra, la + d * NW * 1024, voff + d * NW * 8 * K, k0);
+      else if constexpr (BT)  // a full step: every K row exists, only the column needs the range check
+        dma_lds16(rb, lb + (d - LQA) * NW * 1024, (int)voff_bt, ((d - LQA) * NW * RPB + k0) * ldb);
       else dma_lds16(rb, lb + (d - LQA) * NW * 1024, voff + (d - LQA) * NW * 8 * K, k0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  // A ragged last K step, zero-filled through registers (all threads of the workgroup).
+  // A ragged last K step (all threads of the workgroup): A zero-filled through
+  // registers; B likewise, or (BT) by direct loads whose VGPR offset carries
+  // the row, so K rows past the end read as zero.
   __device__ __forceinline__ void ragged(uint8_t* dst, int kt, int t) const {
     tile_load_zero_fill<BM, 64 * NW>(A, K, m0, m_end, kt * kBK, K, dst, t);
-    tile_load_zero_fill<BN, 64 * NW>(B, K, n0, n_end, kt * kBK, K, dst + BM * kBK, t);
+    if constexpr (BT) {
+      const uint32_t lb = lds_addr(dst + BM * kBK) + w * 1024;
+#pragma unroll
+      for (int d = 0; d < LQB; ++d)
+        dma_lds16(rb, lb + d * NW * 1024, (int)(voff_bt + (uint32_t)((d * NW * RPB + kt * kBK) * ldb)), 0);
+    } else {
+      tile_load_zero_fill<BN, 64 * NW>(B, K, n0, n_end, kt * kBK, K, dst + BM * kBK, t);
+    }
   }
 };
 
@@ -361,7 +405,21 @@ struct MxScaleLoader {
   }
 };
 
-template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, int MODE>
+// LDS transpose read (ds_read_b64_tr_b8), measured lane layout on MI355X:
+// within each group of 16 lanes, lane 8h + c receives byte c of the 8-byte
+// pieces addressed by lanes 2j + h, j = 0..7, as its bytes j.  So when lane
+// 2j + h of a group addresses K row (r0 + j) at column c0 + 8h of a K-major
+// tile, lane 8h + c gets the eight values of column c0 + 8h + c in K rows
+// r0 .. r0 + 7: the K-contiguous fragment a matrix-core operand wants.
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 lds_read_tr8(const uint8_t* p) {
+  typedef __attribute__((address_space(3))) v2i_t lds_v2i;
+  const v2i_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (lds_v2i*)(__attribute__((address_space(3))) uint8_t*)const_cast<uint8_t*>(p));
+  return make_uint2((uint32_t)r[0], (uint32_t)r[1]);
+}
+
+template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, int MODE, bool BT = false>
 __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, int M, int N, int K,
     const float* __restrict__ sinv_a, const float* __restrict__ sinv_b, void* __restrict__ C,
@@ -388,7 +446,8 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
   const int nk = (K + kBK - 1) / kBK;
   const bool ragged_k = (K % kBK) != 0;
 
-  const SlabLoader<BM, BN, NW> slabs(A, m_base, M, B, n_base, N, K, w, lane);
+  const SlabLoader<BM, BN, NW, BT> slabs(A, m_base, M, B, n_base, N, K, w, lane);
+  static_assert(!BT || MODE != kAccumMx, "MXFP8 operands are K-contiguous");
   auto issue_direct = [&](uint8_t* dst, int kt, int g) {
     slabs.issue(dst, kt, g);
     if constexpr (MX) {
@@ -407,6 +466,14 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
   const int swz = lds_swz(rr);
   auto granule = [&](const uint8_t* tile, int row0, int g) {
     return *reinterpret_cast<const uint4*>(tile + (row0 + rr) * kBK + (((g ^ swz) & 7) << 4));
+  };
+  // BT: the lane's role as an address provider of the transpose read (K row
+  // offset jt in 0..7, column half ht) and its 16-lane group gt.
+  const int gt = lane >> 4, jt = (lane & 15) >> 1, ht = lane & 1;
+  // Eight K values of the B tile (BT layout) for the fragment whose 16 columns
+  // start at col0: K rows krow0 + 0..7 of this lane's column.
+  auto bt_piece = [&](const uint8_t* st, int krow0, int col0) {
+    return lds_read_tr8(st + BM * kBK + bt_lds_offset<BN>(krow0 + jt, col0 + 8 * ht));
   };
 
   uint8_t* const s0 = smem;
@@ -510,6 +577,23 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
       const uint4 lo = granule(tile, row0, MX ? hh : 2 * hh), hi = granule(tile, row0, MX ? hh + 4 : 2 * hh + 1);
       return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     };
+    // B fragment of 16 columns starting at col0: the same K order as `frag`
+    // (lane group hh holds K 32hh .. 32hh+31 in register order), taken from the
+    // BT layout as four transpose reads of 8 K rows each.
+    auto frag_b = [&](const uint8_t* st, int col0) {
+      if constexpr (BT) {
+        v8i f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint2 p = bt_piece(st, 32 * gt + 8 * r, col0);
+          f[2 * r] = (int)p.x;
+          f[2 * r + 1] = (int)p.y;
+        }
+        return f;
+      } else {
+        return frag(st + BM * kBK, col0);
+      }
+    };
     static_assert(FN >= kDmaGroups, "one load group per leading B block");
     // A fragments of the step stay in registers; B fragments stream one
     // 16-row block ahead (bf[(j+1)&1] is read while the MFMAs of block j run).
@@ -524,7 +608,7 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
       return *reinterpret_cast<const int*>(st + SLABS + area + (lane >> 4) * rows_in_area + g64 + 4 * (lane & 15));
     };
     auto load_frags = [&](const uint8_t* st) {
-      bf[0] = frag(st + BM * kBK, wn * WTN);
+      bf[0] = frag_b(st, wn * WTN);
       if constexpr (MX) {
         sca = scales4(st, 0, BM, wm * WTM);
 #pragma unroll
@@ -541,7 +625,7 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
       for (int j = 0; j < FN; ++j) {
         if (j < kDmaGroups) dma(j);
         if (j + 1 < FN) {
-          bf[(j + 1) & 1] = frag(st + BM * kBK, wn * WTN + (j + 1) * 16);
+          bf[(j + 1) & 1] = frag_b(st, wn * WTN + (j + 1) * 16);
         }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -586,10 +670,22 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
     // while the MFMAs of granule c run (sub-steps 2c, 2c + 1), so the four
     // waves' LDS reads no longer arrive as one burst that every wave's first
     // MFMA waits behind (1-3 % faster on FC1, identical results).
+    // BT: the B pieces of sub-steps 2c and 2c + 1 come from two transpose reads
+    // (K rows 64 hh + 8s + 0..7 of the lane's column, hh = gt >> 1; lanes
+    // 16 (gt & 1) + 0..15 of each half cover the block's 32 columns).
     uint4 ar[FM][4], br[FN][4];
     auto read_granule = [&](const uint8_t* st, int c) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) br[j][c] = granule(st + BM * kBK, wn * WTN + j * 32, 4 * hh + c);
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (BT) {
+          const int col0 = wn * WTN + j * 32 + 16 * (gt & 1);
+          const uint2 p0 = bt_piece(st, 64 * (gt >> 1) + 16 * c, col0);
+          const uint2 p1 = bt_piece(st, 64 * (gt >> 1) + 16 * c + 8, col0);
+          br[j][c] = make_uint4(p0.x, p0.y, p1.x, p1.y);
+        } else {
+          br[j][c] = granule(st + BM * kBK, wn * WTN + j * 32, 4 * hh + c);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i) ar[i][c] = granule(st, wm * WTM + i * 32, 4 * hh + c);
     };

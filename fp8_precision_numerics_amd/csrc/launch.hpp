@@ -50,7 +50,7 @@ hipError_t launch_amax_update(float* history, int history_len, int32_t* head, co
                               int fmt, float* scale, float* scale_inv, int32_t* status,
                               hipStream_t stream);
 
-hipError_t launch_gemm(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t M, int64_t N,
+hipError_t launch_gemm(const uint8_t* A, int fa, const uint8_t* B, int fb, int b_trans, int64_t M, int64_t N,
                        int64_t K, const float* sinv_a, const float* sinv_b, void* C, int ctype,
                        int accum, hipStream_t stream);
 

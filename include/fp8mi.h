@@ -208,11 +208,17 @@ FP8MI_API int fp8_quantize_update_noalloc(const void* x, int xtype, int64_t rows
  * fp8_gemm — FP8 x FP8 GEMM with FP32 accumulation and the x(1/scale) restore
  * in the epilogue ([TE] §4.2.4; [FMT] "Technical insight").
  *
- *   C[m][n] = ( sum_k dec_fa(A[m][k]) * dec_fb(B[n][k]) ) * sinv_a[0] * sinv_b[0]
+ *   C[m][n] = ( sum_k dec_fa(A[m][k]) * dec_fb(B_kn[k][n]) ) * sinv_a[0] * sinv_b[0]
  *
  * A       device, [M x K] uint8 codes of format fa (K contiguous), 16-B aligned.
- * B       device, [N x K] uint8 codes of format fb (K contiguous: the transpose
- *         of the logical K x N operand, as fp8_quantize's q_t writes it), 16-B aligned.
+ * B       device, uint8 codes of format fb, 16-B aligned:
+ *           b_trans == 0: [N x K], K contiguous (B_kn[k][n] = B[n][k]; the layout
+ *                         fp8_quantize's q_t writes for a weight stored [K x N]);
+ *           b_trans != 0: [K x N], N contiguous (B_kn = B); N must be a multiple
+ *                         of 16 and K * N < 2^31 (else FP8MI_ERR_ALIGN / _SHAPE).
+ *         Both layouts give the same result bit for bit ([TE] §4.2.6: the
+ *         forward and backward GEMMs of a layer take the weight in opposite
+ *         orientations).
  * sinv_a, sinv_b  device, 1 fp32 each: the inverse scales of A and B.
  * C       device, [M x N] of ctype (fp32, or bf16 rounded to nearest even),
  *         16-B aligned.
@@ -223,8 +229,8 @@ FP8MI_API int fp8_quantize_update_noalloc(const void* x, int xtype, int64_t rows
  * M, N >= 0 (M or N == 0 is a no-op).
  * The order in which fp32 partial sums are added is not fixed.
  */
-FP8MI_API int fp8_gemm(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t M, int64_t N, int64_t K,
-             const float* sinv_a, const float* sinv_b, void* C, int ctype, int accum, void* stream);
+FP8MI_API int fp8_gemm(const uint8_t* A, int fa, const uint8_t* B, int fb, int b_trans, int64_t M, int64_t N,
+             int64_t K, const float* sinv_a, const float* sinv_b, void* C, int ctype, int accum, void* stream);
 
 /*
  * fp8_gemm_requant — fp8_gemm whose epilogue re-quantises the result to FP8

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert fm.version() == 700
+    assert fm.version() == 800
     for code in (OK, ENULL, ESHAPE, EALIGN, EFMT, EDTYPE, ELAUNCH, EDEV, EACCUM):
         assert fm.status_string(code) and fm.status_string(code) != "unknown status"
     assert fm.status_string(12345) == "unknown status"
@@ -144,19 +144,23 @@ def test_amax_update_argument_errors(lib):
 
 def test_gemm_argument_errors(lib):
     g = lib.fp8_gemm
-    assert g(A16, 3, A16, 0, 16, 16, 16, A16, A16, A16, 0, 0, None) == EFMT
-    assert g(A16, 0, A16, 0, 16, 16, 16, A16, A16, A16, 4, 0, None) == EDTYPE
-    assert g(A16, 0, A16, 0, 16, 16, 16, A16, A16, A16, 0, 7, None) == EACCUM
-    assert g(A16, 0, A16, 0, 16, 16, 0, A16, A16, A16, 0, 0, None) == ESHAPE
-    assert g(A16, 0, A16, 0, -1, 16, 16, A16, A16, A16, 0, 0, None) == ESHAPE
-    assert g(A16, 0, A16, 0, 1 << 31, 16, 16, A16, A16, A16, 0, 0, None) == ESHAPE
-    assert g(A16, 0, A16, 0, 16, 16, (1 << 23) + 16, A16, A16, A16, 0, 0, None) == ESHAPE   # K limit
-    assert g(A16, 0, A16, 0, 16, 16, 24, A16, A16, A16, 0, 0, None) == EALIGN     # K % 16
-    assert g(None, 0, A16, 0, 16, 16, 16, A16, A16, A16, 0, 0, None) == ENULL
-    assert g(A16, 0, A16, 0, 16, 16, 16, None, A16, A16, 0, 0, None) == ENULL
-    assert g(A8, 0, A16, 0, 16, 16, 16, A16, A16, A16, 0, 0, None) == EALIGN
-    assert g(A16, 0, A16, 0, 16, 16, 16, A16, A16, A8, 0, 0, None) == EALIGN
-    assert g(None, 0, None, 0, 0, 16, 16, None, None, None, 0, 0, None) == OK      # M == 0 is a no-op
+    #        A   fa  B   fb bt  M   N   K   sa   sb   C   ct acc stream
+    assert g(A16, 3, A16, 0, 0, 16, 16, 16, A16, A16, A16, 0, 0, None) == EFMT
+    assert g(A16, 0, A16, 0, 0, 16, 16, 16, A16, A16, A16, 4, 0, None) == EDTYPE
+    assert g(A16, 0, A16, 0, 0, 16, 16, 16, A16, A16, A16, 0, 7, None) == EACCUM
+    assert g(A16, 0, A16, 0, 0, 16, 16, 0, A16, A16, A16, 0, 0, None) == ESHAPE
+    assert g(A16, 0, A16, 0, 0, -1, 16, 16, A16, A16, A16, 0, 0, None) == ESHAPE
+    assert g(A16, 0, A16, 0, 0, 1 << 31, 16, 16, A16, A16, A16, 0, 0, None) == ESHAPE
+    assert g(A16, 0, A16, 0, 0, 16, 16, (1 << 23) + 16, A16, A16, A16, 0, 0, None) == ESHAPE   # K limit
+    assert g(A16, 0, A16, 0, 0, 16, 16, 24, A16, A16, A16, 0, 0, None) == EALIGN     # K % 16
+    assert g(None, 0, A16, 0, 0, 16, 16, 16, A16, A16, A16, 0, 0, None) == ENULL
+    assert g(A16, 0, A16, 0, 0, 16, 16, 16, None, A16, A16, 0, 0, None) == ENULL
+    assert g(A8, 0, A16, 0, 0, 16, 16, 16, A16, A16, A16, 0, 0, None) == EALIGN
+    assert g(A16, 0, A16, 0, 0, 16, 16, 16, A16, A16, A8, 0, 0, None) == EALIGN
+    assert g(None, 0, None, 0, 0, 0, 16, 16, None, None, None, 0, 0, None) == OK      # M == 0 is a no-op
+    # B stored [K x N]: N a multiple of 16, K * N < 2^31
+    assert g(A16, 0, A16, 0, 1, 16, 24, 16, A16, A16, A16, 0, 0, None) == EALIGN
+    assert g(A16, 0, A16, 0, 1, 16, 1 << 20, 1 << 11, A16, A16, A16, 0, 0, None) == ESHAPE
 
 
 def test_blockwise_and_grouped_argument_errors(lib):
@@ -177,7 +181,7 @@ def test_blockwise_and_grouped_argument_errors(lib):
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device path")
 def test_valid_arguments_without_a_device_report_device_error(lib):
-    assert lib.fp8_gemm(A16, 0, A16, 0, 16, 16, 16, A16, A16, A16, 0, 0, None) == EDEV
+    assert lib.fp8_gemm(A16, 0, A16, 0, 0, 16, 16, 16, A16, A16, A16, 0, 0, None) == EDEV
     assert lib.fp8_amax_update(A16, 16, A16, A16, 0, A16, A16, None, None) == EDEV
 
 

@@ -26,14 +26,15 @@ def rand_codes(rng, shape, fmt):
 ACCUMS = ["exact", "mfma_fp8"]
 
 
-def run_gemm(qa, fa, qbT, fb, sa, sb, out="f32", accum="exact"):
+def run_gemm(qa, fa, qbT, fb, sa, sb, out="f32", accum="exact", b_trans=False):
+    """qbT is B as [N x K]; with b_trans the library is handed B as [K x N] instead."""
     dev = device()
     a = torch.from_numpy(np.ascontiguousarray(qa)).to(dev)
-    b = torch.from_numpy(np.ascontiguousarray(qbT)).to(dev)
+    b = torch.from_numpy(np.ascontiguousarray(qbT.T if b_trans else qbT)).to(dev)
     c = torch.empty((qa.shape[0], qbT.shape[0]), dtype=torch.float32 if out == "f32" else torch.bfloat16,
                     device=dev)
     fm.fp8_gemm(a, fa, b, fb, torch.tensor([float(sa)], dtype=torch.float32, device=dev),
-                torch.tensor([float(sb)], dtype=torch.float32, device=dev), c, accum=accum)
+                torch.tensor([float(sb)], dtype=torch.float32, device=dev), c, accum=accum, b_trans=b_trans)
     torch.cuda.synchronize()
     return f32(c)
 
@@ -140,6 +141,52 @@ def test_permutation_selects_columns_exactly(fa, fb, accum):
     c = run_gemm(qa, fa, qbT, fb, np.float32(0.5), np.float32(1), accum=accum)
     want = codec.decode(qa, fa)[:, perm] * codec.decode(cb, fb)[None, :] * 0.5
     assert np.array_equal(c.astype(np.float64), want)
+
+
+# B handed over as [K x N] (N a multiple of 16): small tiles, the 256x256 path
+# with edge tiles, ragged last K steps (400, 144, 272) and a long K.
+BT_SHAPES = [(64, 64, 128), (16, 16, 16), (300, 272, 272), (257, 528, 144), (128, 2048, 256),
+             (1100, 1040, 400), (1024, 1040, 144), (1030, 1024, 4096)]
+
+
+@pytest.mark.parametrize("accum", ACCUMS)
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("fa,fb", PAIRS)
+@pytest.mark.parametrize("M,N,K", BT_SHAPES)
+def test_b_trans_equals_the_k_contiguous_path(M, N, K, fa, fb, out, accum):
+    """B stored [K x N] (b_trans): the kernels read it through the LDS transpose
+    path in the same K order as the [N x K] layout, so both give the same bits;
+    in the exact mode both lie within the method's bound."""
+    rng = np.random.default_rng(M * 7 + N * 5 + K * 3)
+    qa = rand_codes(rng, (M, K), fa)
+    qbT = rand_codes(rng, (N, K), fb)
+    sa, sb = np.float32(0.37), np.float32(2.5e-3)
+    announce(f"b_trans M={M} N={N} K={K} {fa}x{fb}->{out} {accum}")
+    c_nk = run_gemm(qa, fa, qbT, fb, sa, sb, out, accum)
+    c_kn = run_gemm(qa, fa, qbT, fb, sa, sb, out, accum, b_trans=True)
+    assert np.array_equal(c_kn.view(np.uint32), c_nk.view(np.uint32))
+    if accum == "exact" and M * N * K <= (1 << 30):
+        check_within_bound(c_kn, qa, fa, qbT.T, fb, sa, sb, out)
+
+
+def test_b_trans_full_fc1_weight_layout():
+    """The FC1 product with W handed over as stored, [K x N] = 4096 x 16384
+    (no cast-transpose): equal to the product on the cast-transposed weight."""
+    dev = device()
+    rng = np.random.default_rng(99)
+    M, K, N = 8192, 4096, 16384
+    qa = torch.from_numpy(rand_codes(rng, (M, K), "e4m3")).to(dev)
+    qkn = torch.from_numpy(rand_codes(rng, (K, N), "e4m3")).to(dev)
+    qnk = qkn.t().contiguous()
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    announce("b_trans fc1 full size")
+    for accum in ACCUMS:
+        c1 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        c2 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        fm.fp8_gemm(qa, "e4m3", qnk, "e4m3", one, one, c1, accum=accum)
+        fm.fp8_gemm(qa, "e4m3", qkn, "e4m3", one, one, c2, accum=accum, b_trans=True)
+        torch.cuda.synchronize()
+        assert torch.equal(c1.view(torch.int16), c2.view(torch.int16)), accum
 
 
 @pytest.mark.parametrize("fa", ["e4m3", "e5m2"])

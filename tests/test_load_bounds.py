@@ -133,3 +133,95 @@ def test_mx_scale_loads_stay_inside_the_scale_matrices(M, N, K):
                 for r in range(r0, min(rows, r0 + BM)):
                     for blk in range(4 * kt, 4 * kt + 4):
                         assert blk * ld + mx_scale_pos(r) in got, (r, blk)
+
+
+def bt_lds_offset(BN, krow, col):
+    return krow * BN + ((((col >> 4) ^ (krow & 7)) << 4) | (col & 15))
+
+
+def bt_accesses(BN, NW, N, K, n0, kt, ragged):
+    """(krow, col, byte_start, checked_offset, lds_offset) of every direct load of
+    B stored [K x N] for step kt, as SlabLoader<.., BT=true> forms them."""
+    RPB = 1024 // BN
+    LQB = BN // 8 // NW
+    out = []
+    for w in range(NW):
+        for lane in range(64):
+            r = w * RPB + lane // (BN // 16)
+            p = lane % (BN // 16)
+            q = p ^ (r & 7)
+            col = n0 + 16 * q
+            voff_bt = r * N + col if col < N else 0x80000000
+            for d in range(LQB):
+                if ragged:
+                    v = voff_bt + (d * NW * RPB + kt * KBK) * N
+                    s = 0
+                else:
+                    v = voff_bt
+                    s = (d * NW * RPB + kt * KBK) * N
+                assert v < 2 ** 32 and s < 2 ** 31
+                krow = d * NW * RPB + r                    # K row within the step
+                lds = (w + d * NW) * 1024 + lane * 16      # byte offset in the stage's B area
+                out.append((krow, col, v + s, v, lds, p))
+    return out
+
+
+@pytest.mark.parametrize("BN,NW", [(256, 4), (256, 8), (128, 4)])
+@pytest.mark.parametrize("N,K", [(1040, 400), (256, 128), (16, 16), (528, 144), (2048, 4096)])
+def test_bt_slab_loads_stay_inside_b_and_land_in_the_swizzled_layout(BN, NW, N, K):
+    nrec = min(K * N, U32_MAX)
+    nfull = K // KBK
+    for n0 in range(0, N, BN):
+        steps = [(kt, False) for kt in sorted({0, nfull - 1}) if kt >= 0 and nfull > 0]
+        if K % KBK:
+            steps.append((nfull, True))
+        for kt, ragged in steps:
+            fetched = set()
+            for krow, col, start, chk, lds, p in bt_accesses(BN, NW, N, K, n0, kt, ragged):
+                k = kt * KBK + krow
+                if chk + 16 > nrec:
+                    assert col >= N or k >= K, (krow, col)
+                    continue
+                assert col < N and k < K, (krow, col, k)
+                assert start == k * N + col and start + 16 <= K * N
+                assert lds == bt_lds_offset(BN, krow, col - n0)          # swizzled home of this granule
+                fetched.add((krow, col))
+            want = {(kr, c) for kr in range(min(KBK, K - kt * KBK)) for c in range(n0, min(n0 + BN, N), 16)}
+            assert fetched == want
+
+
+@pytest.mark.parametrize("BN", [128, 256])
+def test_bt_transpose_reads_are_bank_conflict_free_and_select_the_right_values(BN):
+    """The fragment reads of the [K x N] B tile: within each 16-lane group the
+    sixteen 8-byte pieces hit 32 distinct LDS banks, and, under the measured
+    lane layout of the transpose read, every lane receives the 8 K values of its
+    own column in K order."""
+    def tr8(addr_of_lane, lds):
+        out = {}
+        for g in range(4):
+            for h in range(2):
+                for c in range(8):
+                    lane = 16 * g + 8 * h + c
+                    out[lane] = [lds[addr_of_lane[16 * g + 2 * j + h] + c] for j in range(8)]
+        return out
+
+    # LDS contents: the (k, n) coordinates of each stored byte, in the BT layout
+    lds = {}
+    for k in range(KBK):
+        for n in range(BN):
+            lds[bt_lds_offset(BN, k, n)] = (k, n)
+    for col0 in range(0, BN, 16):
+        for krow0 in (0, 8, 64, 120):
+            addr = {}
+            for lane in range(64):
+                jt, ht = (lane & 15) >> 1, lane & 1
+                addr[lane] = bt_lds_offset(BN, krow0 + jt, col0 + 8 * ht)
+            for g in range(4):
+                banks = set()
+                for L in range(16):
+                    a = addr[16 * g + L]
+                    banks.update({(a // 4) % 64, (a // 4 + 1) % 64})
+                assert len(banks) == 32
+            got = tr8(addr, lds)
+            for lane, vals in got.items():
+                assert vals == [(krow0 + j, col0 + (lane & 15)) for j in range(8)]
