@@ -281,6 +281,7 @@ def stream_bench(torch, fm, dtype, passes=3):
 
     step = graph_step_ms(True)
     step_separate = graph_step_ms(False)
+    ceiling = hbm_ceiling(torch, fm, xs, q, passes)
     bytes_per_step = R * C * ((2 if dtype == "bf16" else 4) + 1)
     avg = statistics.mean(ms)
     log(f"stream {dtype}: cast + history step {avg * 1e3:.1f} us/call (eager, events per call) = "
@@ -292,7 +293,60 @@ def stream_bench(torch, fm, dtype, passes=3):
             "us_per_step_graph": step * 1e3, "gbs": bytes_per_step / (step * 1e-3) / 1e9,
             "us_per_step_graph_separate_calls": step_separate * 1e3,
             "frac_hbm_peak": bytes_per_step / (step * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "algorithmic_bytes_per_step": bytes_per_step, "per_step": per_step}
+            "algorithmic_bytes_per_step": bytes_per_step, "hbm_ceiling": ceiling, "per_step": per_step}
+
+
+def hbm_ceiling(torch, fm, xs, q, passes=3):
+    """What HBM sustains on cold data, next to the cast: over the 32 resident
+    stream tensors (more than the 256 MB memory-side cache holds), each pass
+    captured once as a HIP graph of 32 back-to-back calls and replayed:
+      copy   a plain device-to-device copy of the tensor (read + write its bytes),
+      read   the amax alone (fp8_quantize with no codes requested: read only),
+      cast   the fused amax + cast with a fixed scale (read, write 1 B per value),
+    each in GB/s of the bytes it must move."""
+    dev = xs[0].device
+    n, eb = xs[0].numel(), xs[0].element_size()
+    dst = torch.empty_like(xs[0])
+    amax = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(fm.QUANTIZE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    scale = torch.ones(1, dtype=torch.float32, device=dev)
+    passes_ = {
+        "copy": (lambda x: dst.copy_(x), 2 * n * eb),
+        "read": (lambda x: fm.fp8_quantize(x, "e4m3", amax=amax, workspace=ws), n * eb),
+        "cast": (lambda x: fm.fp8_quantize(x, "e4m3", scale, q=q, amax=amax, workspace=ws), n * (eb + 1)),
+    }
+    out = {}
+    for name, (fn, nbytes) in passes_.items():
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(xs[0])
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for x in xs:
+                fn(x)
+        graph.replay()
+        torch.cuda.synchronize()
+        per = []
+        for _ in range(passes):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / len(xs))
+        del graph
+        us = statistics.mean(per) * 1e3
+        out[name] = {"us_per_call": us, "bytes_per_call": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9}
+    out["cast_over_copy_gbs"] = out["cast"]["gbs"] / out["copy"]["gbs"]
+    out["cast_over_read_gbs"] = out["cast"]["gbs"] / out["read"]["gbs"]
+    log("hbm ceiling (32 distinct tensors, graph-replayed): " + ", ".join(
+        f"{k} {v['us_per_call']:.1f} us {v['gbs']:.0f} GB/s" for k, v in out.items() if isinstance(v, dict)))
+    del dst, ws
+    return out
 
 
 def linear_bench(torch, fm, iters=10):

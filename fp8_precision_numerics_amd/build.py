@@ -45,9 +45,20 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libfp8mi")
 
 
+# Per-source additions.  grouped_gemm.hip: matrix-core results in ordinary
+# VGPRs instead of accumulation registers.  The exact grouped kernel promotes
+# each 128-deep partial into a separate running sum with a VALU multiply-add;
+# with the partials in accumulation registers every promotion first copies
+# them out (64 extra VALU instructions per step and wave), which made that
+# kernel VALU-bound (measured on MI355X: 943-949 us -> 875-910 us on the MoE
+# shape, identical results).
+EXTRA_FLAGS = {"grouped_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILDDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
