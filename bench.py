@@ -450,7 +450,8 @@ def linear_bench(torch, fm, iters=10):
 def mx_bench(torch, fm, iters=20):
     """MXFP8 on the FC1 shape: the per-32-block quantisation of X (8192 x 4096)
     and of W^T (16384 x 4096), both bf16 -> E4M3 codes + exponent bytes, and the
-    block-scaled GEMM X W^T -> bf16 on the FP8 matrix cores."""
+    GEMM X W^T -> bf16 in both modes: exact (bf16 matrix cores, exact products,
+    fp32 sums) and on the block-scaled FP8 matrix cores."""
     from synth import fc1_forward
 
     dev = torch.device("cuda:0")
@@ -464,24 +465,38 @@ def mx_bench(torch, fm, iters=20):
     qw = torch.empty((N, K), dtype=torch.uint8, device=dev)
     sw = torch.empty((K // 32, fm.mx_scale_ld(N)), dtype=torch.uint8, device=dev)
     c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    t = {k: EventTimer(torch) for k in ("quantize_x", "quantize_w", "gemm")}
+    t = {k: EventTimer(torch) for k in ("quantize_x", "quantize_w", "gemm_exact", "gemm_mfma_fp8",
+                                        "plain_exact_same_codes")}
+    one = torch.ones(1, dtype=torch.float32, device=dev)
     for i in range(iters + 3):
         timed = i >= 3
         with (t["quantize_x"] if timed else _Null()):
             fm.fp8_quantize_mx(X, "e4m3", qx, sx)
         with (t["quantize_w"] if timed else _Null()):
             fm.fp8_quantize_mx(Wt, "e4m3", qw, sw)
-        with (t["gemm"] if timed else _Null()):
-            fm.fp8_gemm_mx(qx, "e4m3", sx, qw, "e4m3", sw, c)
+        with (t["gemm_exact"] if timed else _Null()):
+            fm.fp8_gemm_mx(qx, "e4m3", sx, qw, "e4m3", sw, c, accum="exact")
+        with (t["gemm_mfma_fp8"] if timed else _Null()):
+            fm.fp8_gemm_mx(qx, "e4m3", sx, qw, "e4m3", sw, c, accum="mfma_fp8")
+        # reference: the per-tensor exact GEMM on the same codes (no block scales)
+        with (t["plain_exact_same_codes"] if timed else _Null()):
+            fm.fp8_gemm(qx, "e4m3", qw, "e4m3", one, one, c, accum="exact")
     torch.cuda.synchronize()
     us = {k: statistics.mean(v.ms()) * 1e3 for k, v in t.items()}
     flops = 2.0 * M * N * K
-    res = {"us": us, "gemm_tflops": flops / us["gemm"] / 1e6,
-           "gemm_frac_of_fp8_peak": flops / us["gemm"] / 1e6 / PEAK_FP8_TFLOPS,
+    res = {"us": us,
+           "gemm_exact_tflops": flops / us["gemm_exact"] / 1e6,
+           "gemm_exact_frac_of_fp8_peak": flops / us["gemm_exact"] / 1e6 / PEAK_FP8_TFLOPS,
+           "gemm_exact_frac_of_bf16_peak": flops / us["gemm_exact"] / 1e6 / PEAK_FP16_TFLOPS,
+           "gemm_mfma_fp8_tflops": flops / us["gemm_mfma_fp8"] / 1e6,
+           "gemm_mfma_fp8_frac_of_fp8_peak": flops / us["gemm_mfma_fp8"] / 1e6 / PEAK_FP8_TFLOPS,
            "quantize_x_gbs": M * K * (2 + 1 + 1 / 32) / us["quantize_x"] / 1e3,
            "quantize_w_gbs": N * K * (2 + 1 + 1 / 32) / us["quantize_w"] / 1e3}
     log(f"mxfp8: quantize X {us['quantize_x']:.1f} us ({res['quantize_x_gbs']:.0f} GB/s), W {us['quantize_w']:.1f} us "
-        f"({res['quantize_w_gbs']:.0f} GB/s); gemm {us['gemm']:.1f} us ({res['gemm_tflops']:.0f} TFLOP/s)")
+        f"({res['quantize_w_gbs']:.0f} GB/s); gemm exact {us['gemm_exact']:.1f} us "
+        f"({res['gemm_exact_tflops']:.0f} TFLOP/s), fp8 cores {us['gemm_mfma_fp8']:.1f} us "
+        f"({res['gemm_mfma_fp8_tflops']:.0f} TFLOP/s); per-tensor exact GEMM on the same codes "
+        f"{us['plain_exact_same_codes']:.1f} us")
     del X, Wt, qx, sx, qw, sw, c
     torch.cuda.empty_cache()
     return res

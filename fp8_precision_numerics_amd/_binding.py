@@ -95,7 +95,8 @@ def load_library():
     lib.fp8_dequant_sum.restype = ctypes.c_int
     lib.fp8_quantize_mx.argtypes = [vp, ctypes.c_int, i64, i64, ctypes.c_int, vp, vp, vp]
     lib.fp8_quantize_mx.restype = ctypes.c_int
-    lib.fp8_gemm_mx.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, i64, i64, i64, vp, ctypes.c_int, vp]
+    lib.fp8_gemm_mx.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, i64, i64, i64, vp, ctypes.c_int,
+                                ctypes.c_int, vp]
     lib.fp8_gemm_mx.restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -375,9 +376,11 @@ def fp8_quantize_mx(x, fmt, q, scales, stream=None) -> None:
                                                      _stream(stream)))
 
 
-def fp8_gemm_mx(a, fa, sa, b, fb, sb, c, stream=None) -> None:
+def fp8_gemm_mx(a, fa, sa, b, fb, sb, c, accum="exact", stream=None) -> None:
     """C[M x N] = sum_k (dec(a) 2^(sa - 127)) (dec(b) 2^(sb - 127)) on MXFP8 operands a [M x K], b [N x K];
-    sa [K/32 x mx_scale_ld(M)], sb [K/32 x mx_scale_ld(N)] as fp8_quantize_mx writes them."""
+    sa [K/32 x mx_scale_ld(M)], sb [K/32 x mx_scale_ld(N)] as fp8_quantize_mx writes them.
+    accum: "exact" (exact products, fp32 sums; rows whose block scales span more than 47 give NaN) or
+    "mfma_fp8" (the block-scaled FP8 matrix cores)."""
     lib = load_library()
     dev = a.device
     _check(a, "a", torch.uint8, None, dev)
@@ -392,7 +395,7 @@ def fp8_gemm_mx(a, fa, sa, b, fb, sb, c, stream=None) -> None:
     ctype = F32 if c.dtype == torch.float32 else BF16
     with torch.cuda.device(dev):
         _call("fp8_gemm_mx", lib.fp8_gemm_mx(_p(a), _fmt(fa), _p(sa), _p(b), _fmt(fb), _p(sb), M, N, K, _p(c), ctype,
-                                             _stream(stream)))
+                                             _accum(accum), _stream(stream)))
 
 
 def fp8_quantize_blockwise(x, block_rows, fmt, q, scale_inv, stream=None) -> None:

@@ -238,9 +238,10 @@ int fp8_quantize_mx(const void* x, int xtype, int64_t rows, int64_t cols, int fm
 }
 
 int fp8_gemm_mx(const uint8_t* A, int fa, const uint8_t* sa, const uint8_t* B, int fb, const uint8_t* sb, int64_t M,
-                int64_t N, int64_t K, void* C, int ctype, void* stream) {
+                int64_t N, int64_t K, void* C, int ctype, int accum, void* stream) {
   if (!fmt_ok(fa) || !fmt_ok(fb)) return FP8MI_ERR_FORMAT;
   if (!dtype_ok(ctype)) return FP8MI_ERR_DTYPE;
+  if (!accum_ok(accum)) return FP8MI_ERR_ACCUM;
   if (M < 0 || N < 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxGemmK) return FP8MI_ERR_SHAPE;
   if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N)) return FP8MI_ERR_SHAPE;
   if ((K & 127) != 0) return FP8MI_ERR_ALIGN;
@@ -254,7 +255,7 @@ int fp8_gemm_mx(const uint8_t* A, int fa, const uint8_t* sa, const uint8_t* B, i
     return FP8MI_ERR_ALIGN;
   const int dev = check_device();
   if (dev != FP8MI_OK) return dev;
-  return launched(fp8mi::launch_gemm_mx(A, fa, sa, B, fb, sb, M, N, K, C, ctype, (hipStream_t)stream));
+  return launched(fp8mi::launch_gemm_mx(A, fa, sa, B, fb, sb, M, N, K, C, ctype, accum, (hipStream_t)stream));
 }
 
 int fp8_quantize_blockwise(const void* x, int xtype, int64_t rows, int64_t cols, int32_t block_rows,

@@ -29,7 +29,8 @@ inline hipError_t gemm_dispatch_shape(const uint8_t* A, const uint8_t* B, int64_
                                       const float* sa, const float* sb, void* C, const RequantArgs& rq,
                                       hipStream_t st, const MxScales& mxs = MxScales{nullptr, nullptr}) {
   if (M >= 1024 && N >= 1024) {
-    if constexpr (MODE == kAccumExact) return gemm_run<256, 256, 2, 2, FA, FB, OUT, MODE, BT>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
+    if constexpr (MODE == kAccumExact || MODE == kAccumMxExact)
+      return gemm_run<256, 256, 2, 2, FA, FB, OUT, MODE, BT>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
     else return gemm_run<256, 256, 4, 2, FA, FB, OUT, MODE, BT>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
   }
   return gemm_run<128, 128, 2, 2, FA, FB, OUT, MODE, BT>(A, B, M, N, K, sa, sb, C, rq, st, mxs);

@@ -206,7 +206,7 @@ __device__ __forceinline__ void wait_loads_and_barrier() {
 template <class Issue, class Ragged, class Frags, class Compute, class Hint>
 __device__ __forceinline__ void run_main_loop(uint8_t* s0, uint8_t* s1, int nfull, int nk, bool ragged_k,
                                               Issue& issue_direct, Ragged& stage_ragged, Frags& load_frags,
-                                              Compute& compute, Hint& interleave) {
+                                              Compute& compute, Hint& interleave, bool first_issued = false) {
   // The loads of step kt+1 go out in groups between the first MFMA blocks of
   // step kt (the hook `dma(g)`): issued all at once they back up the wave's
   // memory-instruction queue and stall its MFMAs.  The MFMAs stay inside their
@@ -221,7 +221,8 @@ __device__ __forceinline__ void run_main_loop(uint8_t* s0, uint8_t* s1, int nful
   };
   auto no_dma = [](int) {};
   if (nfull > 0) {
-    for (int g = 0; g < kDmaGroups; ++g) issue_direct(s0, 0, g);
+    if (!first_issued)
+      for (int g = 0; g < kDmaGroups; ++g) issue_direct(s0, 0, g);
     wait_loads_and_barrier();
     load_frags(s0);
   } else {
@@ -378,32 +379,132 @@ __device__ __forceinline__ void publish_requant_stats(uint32_t amax_bits_lane, u
 __host__ __device__ constexpr int64_t mx_scale_ld(int64_t rows) { return (rows + 63) / 64 * 64; }
 __host__ __device__ constexpr int64_t mx_scale_pos(int64_t r) { return (r & ~int64_t(63)) | ((r & 15) << 2) | ((r >> 4) & 3); }
 
+// With fewer lanes than dwords (4-wave tiles: 256 lanes for 512 dwords) each
+// lane issues PER loads, entry e + u * 64 * NW for u < PER.  BM is a multiple
+// of 64, so each wave's load u is all A or all B (a wave-uniform choice).
 template <int BM, int BN, int NW>
 struct MxScaleLoader {
-  static_assert(BM + BN == 64 * NW && BM % 64 == 0, "one dword of scales per lane");
-  __amdgpu_buffer_rsrc_t r;
-  int voff, w, step;
+  static constexpr int PER = (BM + BN) / (64 * NW);
+  static_assert(PER >= 1 && BM + BN == PER * 64 * NW && BM % 64 == 0, "whole dwords of scales per lane");
+  __amdgpu_buffer_rsrc_t r[PER];
+  int voff[PER], step[PER];
+  int w;
   __device__ __forceinline__ MxScaleLoader(const MxScales& sx, int64_t m0, int64_t M, int64_t n0, int64_t N, int K,
                                            int w_, int lane)
       : w(w_) {
-    const int e = w * 64 + lane;
-    if (w < BM / 64) {
-      const int64_t ld = mx_scale_ld(M);
-      r = operand_rsrc(sx.a, K / 32, ld);
-      voff = (int)((e / (BM / 4)) * ld + m0 + 4 * (e % (BM / 4)));
-      step = (int)(4 * ld);
-    } else {
-      const int64_t ld = mx_scale_ld(N);
-      const int f = e - BM;
-      r = operand_rsrc(sx.b, K / 32, ld);
-      voff = (int)((f / (BN / 4)) * ld + n0 + 4 * (f % (BN / 4)));
-      step = (int)(4 * ld);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = w * 64 + lane + u * 64 * NW;
+      if ((w + u * NW) * 64 < BM) {  // uniform over the wave
+        const int64_t ld = mx_scale_ld(M);
+        r[u] = operand_rsrc(sx.a, K / 32, ld);
+        voff[u] = (int)((e / (BM / 4)) * ld + m0 + 4 * (e % (BM / 4)));
+        step[u] = (int)(4 * ld);
+      } else {
+        const int64_t ld = mx_scale_ld(N);
+        const int f = e - BM;
+        r[u] = operand_rsrc(sx.b, K / 32, ld);
+        voff[u] = (int)((f / (BN / 4)) * ld + n0 + 4 * (f % (BN / 4)));
+        step[u] = (int)(4 * ld);
+      }
     }
   }
   __device__ __forceinline__ void issue(uint8_t* scale_area, int kt) const {
-    dma_lds4(r, lds_addr(scale_area) + w * 256, voff + kt * step, 0);
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      dma_lds4(r[u], lds_addr(scale_area) + (w + u * NW) * 256, voff[u] + kt * step[u], 0);
   }
 };
+
+// kAccumMxExact: the reference exponent of every row of the tile and whether
+// the row's block exponents fit the exact path.  Scale codes c (2^(c - 127))
+// are scanned over all K/32 blocks; R = the row's largest code.  A block of
+// code c is widened with the factor 2^(c - R), so the smallest nonzero value
+// of the row becomes at least 2^-16 (the smallest E5M2 subnormal) times
+// 2^-(span), span = R - (the row's smallest code); with span <= kMxExactSpan
+// for both operands every nonzero product is at least 2^-126 (an fp32 normal
+// number) and at most 57344^2, so the fp32 accumulation sees exact products.
+// Rows outside that window get a NaN factor: their outputs are NaN rather than
+// silently inexact.  Output in LDS (refs): bytes [0, BM) and [BM, BM + BN) the
+// codes R of the A and B rows, floats at refs + 512: 2^(R - 127) or NaN.
+constexpr int kMxExactSpan = 47;
+constexpr int kMxRefBytes = 512 + 4 * 512 + 16 * 256;  // codes, factors, reduction scratch (256 threads)
+
+template <int BM, int BN, int NT>
+__device__ __forceinline__ void mx_row_refs(const MxScales& sx, int64_t m0, int64_t M, int64_t n0, int64_t N, int K,
+                                            int t, uint8_t* scratch, uint8_t* refs) {
+  static_assert(BM + BN <= 512, "reference area");
+  constexpr int DW = (BM + BN) / 4;  // dwords of one K block's codes for the tile (A then B)
+  static_assert(NT % DW == 0, "whole blocks per pass");
+  constexpr int LANES = NT / DW;     // blocks scanned side by side
+  const int nb = K / 32;
+  const int d = t % DW, b0 = t / DW;
+  const bool is_a = d < BM / 4;
+  const int64_t ld = is_a ? mx_scale_ld(M) : mx_scale_ld(N);
+  const __amdgpu_buffer_rsrc_t r = operand_rsrc(is_a ? sx.a : sx.b, nb, ld);
+  const int voff0 = (int)(is_a ? m0 + 4 * d : n0 + 4 * (d - BM / 4));
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 mx_lo = {0, 0}, mx_hi = {0, 0}, mn_lo = {255, 255}, mn_hi = {255, 255};
+  // U loads in flight per thread before any is used: each is a round trip to
+  // L2 or beyond, and one at a time they dominated the tile's start.
+  constexpr int U = 32;
+  for (int b = b0; b < nb; b += LANES * U) {
+    uint32_t w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int bb = b + u * LANES;
+      w[u] = bb < nb ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, voff0 + (int)(bb * ld), 0, 0) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (b + u * LANES >= nb) break;
+      const u16x2 lo = __builtin_bit_cast(u16x2, w[u] & 0x00FF00FFu);
+      const u16x2 hi = __builtin_bit_cast(u16x2, (w[u] >> 8) & 0x00FF00FFu);
+      mx_lo = __builtin_elementwise_max(mx_lo, lo);
+      mx_hi = __builtin_elementwise_max(mx_hi, hi);
+      mn_lo = __builtin_elementwise_min(mn_lo, lo);
+      mn_hi = __builtin_elementwise_min(mn_hi, hi);
+    }
+  }
+  // combine the LANES partial results of each dword through LDS
+  static_assert(NT * 16 <= 16 * 256, "reduction scratch");
+  uint32_t* part = reinterpret_cast<uint32_t*>(scratch);
+  part[4 * t + 0] = __builtin_bit_cast(uint32_t, mx_lo);
+  part[4 * t + 1] = __builtin_bit_cast(uint32_t, mx_hi);
+  part[4 * t + 2] = __builtin_bit_cast(uint32_t, mn_lo);
+  part[4 * t + 3] = __builtin_bit_cast(uint32_t, mn_hi);
+  __syncthreads();
+  if (t < DW) {
+    uint32_t mxb[4] = {0, 0, 0, 0}, mnb[4] = {255, 255, 255, 255};
+    for (int l = 0; l < LANES; ++l) {
+      const uint32_t* p = part + 4 * (t + l * DW);
+      const uint32_t v[4] = {p[0] & 0xFFu, p[1] & 0xFFu, p[0] >> 16, p[1] >> 16};      // max of bytes 0, 1, 2, 3
+      const uint32_t u[4] = {p[2] & 0xFFu, p[3] & 0xFFu, p[2] >> 16, p[3] >> 16};      // min of bytes 0, 1, 2, 3
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        mxb[i] = v[i] > mxb[i] ? v[i] : mxb[i];
+        mnb[i] = u[i] < mnb[i] ? u[i] : mnb[i];
+      }
+    }
+    // byte i of the dword at tile position 4 d' holds the row whose position
+    // within its 64-row group is 4 (d' % 16) + i: row (pos & ~63) | (i << 4) | (d' % 16)
+    const bool a_side = t < BM / 4;
+    const int dd = a_side ? t : t - BM / 4;
+    const int64_t rows_valid = a_side ? M - m0 : N - n0;
+    float* fac = reinterpret_cast<float*>(refs + 512);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pos = 4 * dd + i;
+      const int row = (pos & ~63) | (i << 4) | ((pos >> 2) & 15);
+      const int slot = (a_side ? 0 : BM) + row;
+      refs[slot] = (uint8_t)mxb[i];
+      const bool ok = row >= rows_valid || (int)(mxb[i] - mnb[i]) <= kMxExactSpan;
+      fac[slot] = ok ? (mxb[i] ? __builtin_bit_cast(float, mxb[i] << 23) : __builtin_bit_cast(float, 0x00400000u))
+                     : __builtin_nanf("");
+    }
+  }
+  __syncthreads();
+}
 
 // LDS transpose read (ds_read_b64_tr_b8), measured lane layout on MI355X:
 // within each group of 16 lanes, lane 8h + c receives byte c of the 8-byte
@@ -428,14 +529,16 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
   constexpr int WTM = BM / WM, WTN = BN / WN;
   // Output block of one matrix-core instruction: 16x16 (FP8 paths), 32x32 (fp16 path).
   constexpr bool MX = MODE == kAccumMx;
-  constexpr int BLK = MODE == kAccumExact ? 32 : 16;
+  constexpr bool MXE = MODE == kAccumMxExact;
+  constexpr bool MXS = MX || MXE;  // stages carry the step's E8M0 block scales
+  constexpr int BLK = (MODE == kAccumExact || MXE) ? 32 : 16;
   constexpr int FM = WTM / BLK, FN = WTN / BLK;
   static_assert(FM >= 1 && FN >= 1 && WTM % BLK == 0 && WTN % BLK == 0, "wave tile shape");
   // A stage: the A slab, the B slab, and (MXFP8) their block scales.
   constexpr int SLABS = (BM + BN) * kBK;
-  constexpr int STAGE = SLABS + (MX ? (BM + BN) * 4 : 0);
+  constexpr int STAGE = SLABS + (MXS ? (BM + BN) * 4 : 0);
   static_assert(STAGE % 1024 == 0, "stages keep the slabs' 1 KiB alignment");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE + (MXE ? kMxRefBytes : 0)];
 
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, &tm, &tn);
@@ -447,10 +550,10 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
   const bool ragged_k = (K % kBK) != 0;
 
   const SlabLoader<BM, BN, NW, BT> slabs(A, m_base, M, B, n_base, N, K, w, lane);
-  static_assert(!BT || MODE != kAccumMx, "MXFP8 operands are K-contiguous");
+  static_assert(!BT || !MXS, "MXFP8 operands are K-contiguous");
   auto issue_direct = [&](uint8_t* dst, int kt, int g) {
     slabs.issue(dst, kt, g);
-    if constexpr (MX) {
+    if constexpr (MXS) {
       if (g == 0) MxScaleLoader<BM, BN, NW>(mxs, m_base, M, n_base, N, K, w, lane).issue(dst + SLABS, kt);
     }
   };
@@ -660,11 +763,70 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
       }
     });
   } else {
+    // fp16 path (kAccumExact) or bf16 path with block scales (kAccumMxExact)
+    using H8 = std::conditional_t<MXE, v8bf, v8h>;
     v16f acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = (v16f){};
+    uint8_t* const refs = smem + 2 * STAGE;  // kAccumMxExact: the rows' reference codes and factors
+    // kAccumMxExact: the conversion factors 2^(c - R) of the lane's rows for
+    // block 2 hh + h of the current step (c from the stage's scale bytes, R
+    // the row's reference code).  Sub-steps 4h .. 4h + 3 lie in that block.
+    // The lane's rows are 32 apart: rows i and i + 1 (i even) of a 64-row
+    // group share one scale dword (bytes l >> 4 and 2 + (l >> 4), l = lane & 31),
+    // so a half-step's codes take FM / 2 + FN / 2 dword reads.  The reference
+    // codes do not change over the tile: kept packed, one byte per row.
+    static_assert(!MXE || (FM % 2 == 0 && FN % 2 == 0 && WTM % 64 == 0 && WTN % 64 == 0), "row pairs per dword");
+    float fa[FM], fb[FN];
+    uint32_t ref_a = 0, ref_b = 0;
+    const int sel = 8 * ((lane >> 4) & 1);
+    if constexpr (MXE) {
+      // the first step's slabs and scales load while the rows' references are
+      // found (K is a multiple of 128 here, so step 0 is a full step)
+      for (int g = 0; g < kDmaGroups; ++g) issue_direct(s0, 0, g);
+      mx_row_refs<BM, BN, NT>(mxs, m_base, M, n_base, N, K, t, refs + 512 + 4 * 512, refs);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) ref_a |= (uint32_t)refs[wm * WTM + i * 32 + (lane & 31)] << (8 * i);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) ref_b |= (uint32_t)refs[BM + wn * WTN + j * 32 + (lane & 31)] << (8 * j);
+    }
+    auto codes_dword = [&](const uint8_t* st, int area, int rows_in_area, int h, int row0) {
+      return *reinterpret_cast<const uint32_t*>(st + SLABS + area + (2 * hh + h) * rows_in_area + row0 +
+                                                4 * (lane & 15));
+    };
+    auto to_factor = [&](uint32_t code, uint32_t ref) {
+      return __builtin_bit_cast(float, (code - ref + 127u) << 23);
+    };
+    auto load_fa = [&](const uint8_t* st, int h) {
+#pragma unroll
+      for (int i = 0; i < FM; i += 2) {
+        const uint32_t d = codes_dword(st, 0, BM, h, wm * WTM + i * 32);
+        fa[i] = to_factor((d >> sel) & 0xFFu, (ref_a >> (8 * i)) & 0xFFu);
+        fa[i + 1] = to_factor((d >> (sel + 16)) & 0xFFu, (ref_a >> (8 * i + 8)) & 0xFFu);
+      }
+    };
+    auto load_fb = [&](const uint8_t* st, int h) {
+#pragma unroll
+      for (int j = 0; j < FN; j += 2) {
+        const uint32_t d = codes_dword(st, 4 * BM, BN, h, wn * WTN + j * 32);
+        fb[j] = to_factor((d >> sel) & 0xFFu, (ref_b >> (8 * j)) & 0xFFu);
+        fb[j + 1] = to_factor((d >> (sel + 16)) & 0xFFu, (ref_b >> (8 * j + 8)) & 0xFFu);
+      }
+    };
+    auto widen_a = [&](uint32_t w0, uint32_t w1, int i) -> H8 {
+      if constexpr (MXE) return widen8_scaled_bf16<FA>(w0, w1, fa[i]);
+      else return widen8<FA>(w0, w1);
+    };
+    auto widen_b = [&](uint32_t w0, uint32_t w1, int j) -> H8 {
+      if constexpr (MXE) return widen8_scaled_bf16<FB>(w0, w1, fb[j]);
+      else return widen8<FB>(w0, w1);
+    };
+    auto mfma = [&](const H8& b, const H8& a, const v16f& c) {
+      if constexpr (MXE) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
+      else return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
+    };
     // Raw FP8 fragments of the whole step: 4 granules (64 bytes) per block.
     // Only granule 0 is read right after the barrier; granule c + 1 is read
     // while the MFMAs of granule c run (sub-steps 2c, 2c + 1), so the four
@@ -697,15 +859,19 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
     // sub-step ahead, and the scheduling groups place two conversions (the
     // remaining A blocks', then the next sub-step's B blocks') after each
     // MFMA, inside its shadow (2-3 % faster on FC1, identical results).
-    auto cvt_b = [&](int s, v8h* out) {
+    auto cvt_b = [&](int s, H8* out) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const uint4 g = br[j][s >> 1];
-        out[j] = (s & 1) ? widen8<FB>(g.z, g.w) : widen8<FB>(g.x, g.y);
+        out[j] = (s & 1) ? widen_b(g.z, g.w, j) : widen_b(g.x, g.y, j);
       }
     };
     auto compute = [&](const uint8_t* st, auto&& dma) {
-      v8h bb[2][FN];
+      H8 bb[2][FN];
+      if constexpr (MXE) {
+        load_fa(st, 0);
+        load_fb(st, 0);
+      }
       cvt_b(0, bb[0]);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
@@ -714,13 +880,22 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
           read_granule(st, (s >> 1) + 1);
           __builtin_amdgcn_sched_barrier(0);
         }
-        const v8h* bh = bb[s & 1];
+        const H8* bh = bb[s & 1];
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           const uint4 g = ar[i][s >> 1];
-          const v8h ah = (s & 1) ? widen8<FA>(g.z, g.w) : widen8<FA>(g.x, g.y);
+          const H8 ah = (s & 1) ? widen_a(g.z, g.w, i) : widen_a(g.x, g.y, i);
 #pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bh[j], ah, acc[i][j], 0, 0, 0);
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma(bh[j], ah, acc[i][j]);
+        }
+        if constexpr (MXE) {
+          // the second block's factors: after the last use of the first's
+          // (sub-step 3's A conversions), before cvt_b(4); the LDS reads are
+          // free to move up over this sub-step's MFMAs
+          if (s == 3) {
+            load_fa(st, 1);
+            load_fb(st, 1);
+          }
         }
         if (s + 1 < 8) cvt_b(s + 1, bb[(s + 1) & 1]);
         __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
@@ -733,22 +908,32 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
       }
     };
     auto interleave = [&]() {};
-    run_main_loop(s0, s1, nfull, nk, ragged_k, issue_direct, stage_ragged, load_frags, compute, interleave);
+    run_main_loop(s0, s1, nfull, nk, ragged_k, issue_direct, stage_ragged, load_frags, compute, interleave, MXE);
 
     // Lane l holds row m = l & 31 of each 32x32 block (the A operand went
     // second) and columns n = 8g + 4(l >> 5) + 0..3 in registers 4g..4g+3.
-    const float sc = sinv_a[0] * sinv_b[0];
+    // kAccumMxExact: the result is acc * 2^(R_a - 127) * 2^(R_b - 127), in
+    // that order (each step exact unless the result leaves fp32's range).
+    const float sc = MXE ? 1.0f : sinv_a[0] * sinv_b[0];
+    const float* fac = reinterpret_cast<const float*>(refs + 512);
     write_tile_checked([&](int r_lo, int r_hi, auto& tw, auto mask) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int r = wm * WTM + i * 32 + (lane & 31);
         if (r < r_lo || r >= r_hi) continue;
+        const float fr = MXE ? fac[r] : sc;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
+            const int n = wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
             const v4f v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-            emit4(tw, r, r_lo, wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5), v * sc, mask);
+            if constexpr (MXE) {
+              const v4f fc = *reinterpret_cast<const v4f*>(fac + BM + n);
+              emit4(tw, r, r_lo, n, (v * fr) * fc, mask);
+            } else {
+              emit4(tw, r, r_lo, n, v * sc, mask);
+            }
           }
       }
     });

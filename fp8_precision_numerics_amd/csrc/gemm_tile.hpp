@@ -50,10 +50,17 @@ namespace fp8mi {
 constexpr int kBK = 128;  // K bytes per main-loop step
 // kAccumMx: the FP8 instruction with a power-of-two (E8M0) scale per 32-deep K
 // block of each operand row (MXFP8), applied by the instruction itself.
-enum : int { kAccumExact = 0, kAccumMfma8 = 1, kAccumMx = 2 };
+// kAccumMxExact: MXFP8 operands with every product exact and fp32 sums: the
+// codes are widened to bf16 with the block's power of two relative to the
+// row's largest block exponent folded into the conversion (exact: bf16 keeps
+// 8 significant bits and fp32's exponent range), contracted with
+// V_MFMA_F32_32X32X16_BF16, and the two rows' reference powers of two are
+// applied in the epilogue.
+enum : int { kAccumExact = 0, kAccumMfma8 = 1, kAccumMx = 2, kAccumMxExact = 3 };
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ int lds_swz(int row) { return (row & 6) | ((row >> 3) & 1); }
 __device__ __forceinline__ int lds_granule(int row, int g) { return row * kBK + (((g ^ lds_swz(row)) & 7) << 4); }
@@ -108,6 +115,27 @@ __device__ __forceinline__ v8h widen8(uint32_t w0, uint32_t w1) {
     d = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w1, 1.0f, true);
   }
   return (v8h){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Eight FP8 codes (bytes of w0 then w1) times `scale` (a power of two),
+// converted to bf16.  Measured on MI355X: exact for every code of both formats
+// at every power of two from 2^-90 to 2^90 (the product has at most 4
+// significant bits and stays inside bf16's normal range there).
+template <int F>
+__device__ __forceinline__ v8bf widen8_scaled_bf16(uint32_t w0, uint32_t w1, float scale) {
+  v2bf a, b, c, d;
+  if constexpr (F == kE4M3) {
+    a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, false);
+    b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, true);
+    c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, false);
+    d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, true);
+  } else {
+    a = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, scale, false);
+    b = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, scale, true);
+    c = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, scale, false);
+    d = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, scale, true);
+  }
+  return (v8bf){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // A ROWS x 128-byte slab (rows row0.. of a row-major byte matrix with row

@@ -74,6 +74,6 @@ hipError_t launch_quantize_mx(const void* x, int xtype, int64_t rows, int64_t co
                               uint8_t* scales, hipStream_t stream);
 
 hipError_t launch_gemm_mx(const uint8_t* A, int fa, const uint8_t* sa, const uint8_t* B, int fb, const uint8_t* sb,
-                          int64_t M, int64_t N, int64_t K, void* C, int ctype, hipStream_t stream);
+                          int64_t M, int64_t N, int64_t K, void* C, int ctype, int accum, hipStream_t stream);
 
 }  // namespace fp8mi

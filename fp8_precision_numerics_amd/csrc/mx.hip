@@ -199,10 +199,15 @@ hipError_t launch_quantize_mx(const void* x, int xtype, int64_t rows, int64_t co
 }
 
 hipError_t launch_gemm_mx(const uint8_t* A, int fa, const uint8_t* sa, const uint8_t* B, int fb, const uint8_t* sb,
-                          int64_t M, int64_t N, int64_t K, void* C, int ctype, hipStream_t stream) {
+                          int64_t M, int64_t N, int64_t K, void* C, int ctype, int accum, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const RequantArgs none{nullptr, nullptr, nullptr};
   const MxScales mxs{sa, sb};
+  if (accum == kAccumExact) {
+    if (ctype == kBF16)
+      return gemm_dispatch_fmt<kBF16, kAccumMxExact>(A, fa, B, fb, M, N, K, nullptr, nullptr, C, none, stream, mxs);
+    return gemm_dispatch_fmt<kF32, kAccumMxExact>(A, fa, B, fb, M, N, K, nullptr, nullptr, C, none, stream, mxs);
+  }
   if (ctype == kBF16)
     return gemm_dispatch_fmt<kBF16, kAccumMx>(A, fa, B, fb, M, N, K, nullptr, nullptr, C, none, stream, mxs);
   return gemm_dispatch_fmt<kF32, kAccumMx>(A, fa, B, fb, M, N, K, nullptr, nullptr, C, none, stream, mxs);

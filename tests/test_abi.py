@@ -109,15 +109,16 @@ def test_mx_argument_errors(lib):
     assert qm(A16, 0, 4, 64, 0, A16, None, None) == ENULL
     assert qm(A8, 0, 4, 64, 0, A16, A16, None) == EALIGN
     assert qm(None, 0, 0, 64, 0, None, None, None) == OK           # empty
-    #        A    fa  sa   B    fb  sb   M   N   K    C   ct stream
-    assert gm(A16, 0, A16, A16, 3, A16, 16, 16, 128, A16, 0, None) == EFMT
-    assert gm(A16, 0, A16, A16, 0, A16, 16, 16, 128, A16, 4, None) == EDTYPE
-    assert gm(A16, 0, A16, A16, 0, A16, 16, 16, 96, A16, 0, None) == EALIGN   # 128 | K
-    assert gm(A16, 0, None, A16, 0, A16, 16, 16, 128, A16, 0, None) == ENULL
-    assert gm(A16, 0, ctypes.c_void_p(0x10002), A16, 0, A16, 16, 16, 128, A16, 0, None) == EALIGN
-    assert gm(A16, 0, A16, A16, 0, A16, 16, 16, 1 << 24, A16, 0, None) == ESHAPE
+    #        A    fa  sa   B    fb  sb   M   N   K    C   ct acc stream
+    assert gm(A16, 0, A16, A16, 3, A16, 16, 16, 128, A16, 0, 0, None) == EFMT
+    assert gm(A16, 0, A16, A16, 0, A16, 16, 16, 128, A16, 4, 0, None) == EDTYPE
+    assert gm(A16, 0, A16, A16, 0, A16, 16, 16, 128, A16, 0, 5, None) == EACCUM
+    assert gm(A16, 0, A16, A16, 0, A16, 16, 16, 96, A16, 0, 0, None) == EALIGN   # 128 | K
+    assert gm(A16, 0, None, A16, 0, A16, 16, 16, 128, A16, 0, 0, None) == ENULL
+    assert gm(A16, 0, ctypes.c_void_p(0x10002), A16, 0, A16, 16, 16, 128, A16, 0, 0, None) == EALIGN
+    assert gm(A16, 0, A16, A16, 0, A16, 16, 16, 1 << 24, A16, 0, 0, None) == ESHAPE
     # the A scale matrix (K/32 x 2^20 bytes = 4 GiB) would not fit a 32-bit load offset
-    assert gm(A16, 0, A16, A16, 0, A16, 1 << 20, 16, 1 << 17, A16, 0, None) == ESHAPE
+    assert gm(A16, 0, A16, A16, 0, A16, 1 << 20, 16, 1 << 17, A16, 0, 0, None) == ESHAPE
 
 
 def test_quantize_update_argument_errors(lib):

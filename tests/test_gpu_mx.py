@@ -1,6 +1,7 @@
 """GPU parity: MXFP8 quantisation (fp8_quantize_mx) bit for bit against the
-oracle, and the MXFP8 GEMM (fp8_gemm_mx) within the error model of the FP8
-matrix cores on the oracle's exact product."""
+oracle; the MXFP8 GEMM (fp8_gemm_mx) in the exact mode within the method's
+1e-5 * sum|ab| of the oracle's product, and in the FP8-matrix-core mode within
+the error model of that instruction."""
 
 import numpy as np
 import pytest
@@ -122,12 +123,13 @@ def test_gemm_mx_within_error_model(M, N, K, fa, fb, out):
     dev = device()
     c = torch.empty((M, N), dtype=torch.float32 if out == "f32" else torch.bfloat16, device=dev)
     fm.fp8_gemm_mx(torch.from_numpy(qa).to(dev), fa, _dev_scales(sa, dev), torch.from_numpy(qb).to(dev), fb,
-                   _dev_scales(sb, dev, pad=255), c)
+                   _dev_scales(sb, dev, pad=255), c, accum="mfma_fp8")
     torch.cuda.synchronize()
     _check_mx(f32(c), qa, sa, fa, qb, sb, fb, out)
 
 
-def test_gemm_mx_block_scales_select_blocks():
+@pytest.mark.parametrize("accum", ["exact", "mfma_fp8"])
+def test_gemm_mx_block_scales_select_blocks(accum):
     """Closed form: all codes 1.0; A's block b of row m has exponent code 127 + b,
     B's block b of row n has 127 - b + (n % 3): C[m, n] = 32 * nb * 2^(n % 3),
     exact (every product a power of two, sums of equal terms)."""
@@ -140,7 +142,7 @@ def test_gemm_mx_block_scales_select_blocks():
     sb = (127 - np.arange(nb)[None, :] + (np.arange(N) % 3)[:, None]).astype(np.uint8)
     c = torch.empty((M, N), dtype=torch.float32, device=dev)
     fm.fp8_gemm_mx(torch.from_numpy(qa).to(dev), "e4m3", _dev_scales(sa, dev), torch.from_numpy(qb).to(dev),
-                   "e4m3", _dev_scales(sb, dev), c)
+                   "e4m3", _dev_scales(sb, dev), c, accum=accum)
     torch.cuda.synchronize()
     want = 32.0 * nb * 2.0 ** (np.arange(N) % 3)
     assert np.array_equal(f32(c), np.tile(want, (M, 1)).astype(np.float32))
@@ -164,7 +166,9 @@ def test_fc1_mx_full_size():
     fm.fp8_quantize_mx(to_device(X, dev), "e4m3", qx, sx)
     fm.fp8_quantize_mx(to_device(W, dev), "e4m3", qw, sw)
     c = torch.empty((8192, 16384), dtype=torch.float32, device=dev)
-    fm.fp8_gemm_mx(qx, "e4m3", sx, qw, "e4m3", sw, c)
+    fm.fp8_gemm_mx(qx, "e4m3", sx, qw, "e4m3", sw, c, accum="mfma_fp8")
+    ce = torch.empty((8192, 16384), dtype=torch.bfloat16, device=dev)
+    fm.fp8_gemm_mx(qx, "e4m3", sx, qw, "e4m3", sw, ce, accum="exact")
     torch.cuda.synchronize()
     rng = np.random.default_rng(71)
     rows_x = np.concatenate([rng.choice(8192, 24, replace=False), [0, 8191]])
@@ -177,3 +181,73 @@ def test_fc1_mx_full_size():
     assert np.array_equal(qw_h, wqw) and np.array_equal(sw_h, wsw)
     got = f32(c)[np.ix_(rows_x, rows_w)]
     _check_mx(got, wqx, wsx, "e4m3", wqw, wsw, "e4m3", "f32")
+    # the exact mode on the same operands: the method's bound (bf16 output)
+    _check_mx_exact(f32(ce)[np.ix_(rows_x, rows_w)], wqx, wsx, "e4m3", wqw, wsw, "e4m3", "bf16")
+
+
+def _check_mx_exact(c_gpu, qa, sa, fa, qb, sb, fb, out, nan_rows=(), nan_cols=()):
+    """The method's tolerance on the dequantised operands: |C - C64| <= 1e-5 *
+    sum_k |a_k b_k| (bf16: the bracket of C64 -+ that bound); rows / columns
+    listed as outside the exact path's exponent window must be NaN."""
+    c64 = mx.mx_gemm(qa, sa, fa, qb, sb, fb)
+    bound = 1e-5 * (np.abs(mx.dequant_mx(qa, sa, fa)) @ np.abs(mx.dequant_mx(qb, sb, fb)).T)
+    mask = np.zeros(c64.shape, dtype=bool)
+    mask[list(nan_rows), :] = True
+    mask[:, list(nan_cols)] = True
+    assert np.isnan(c_gpu[mask]).all()
+    c_gpu, c64, bound = c_gpu[~mask], c64[~mask], bound[~mask]
+    if out == "f32":
+        err = np.abs(c_gpu.astype(np.float64) - c64)
+        bad = np.flatnonzero(err > bound)
+        assert bad.size == 0, (bad[:5], err[bad[0]], bound[bad[0]])
+    else:
+        lo, hi = gemm.bf16_bracket(c64, bound)
+        ok = (c_gpu >= lo) & (c_gpu <= hi)
+        assert ok.all(), np.flatnonzero(~ok)[:5]
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2")])
+@pytest.mark.parametrize("M,N,K", [(64, 64, 128), (1, 1, 128), (300, 260, 256), (257, 513, 384), (1100, 1030, 512),
+                                   (1024, 1040, 640)])
+def test_gemm_mx_exact_within_method_bound(M, N, K, fa, fb, out):
+    """Exact mode: random codes over every finite value (subnormals included)
+    with random block exponents 2^-15 .. 2^14 on both operands (the window of
+    the exact path is 47 binades per row): within 1e-5 * sum|ab| everywhere."""
+    announce(f"gemm_mx exact {M}x{N}x{K} {fa}x{fb} {out}")
+    rng = np.random.default_rng(M + 3 * N + 7 * K + 1)
+    qa, sa = _rand_mx(rng, M, K, fa)
+    qb, sb = _rand_mx(rng, N, K, fb)
+    dev = device()
+    c = torch.empty((M, N), dtype=torch.float32 if out == "f32" else torch.bfloat16, device=dev)
+    fm.fp8_gemm_mx(torch.from_numpy(qa).to(dev), fa, _dev_scales(sa, dev), torch.from_numpy(qb).to(dev), fb,
+                   _dev_scales(sb, dev, pad=255), c, accum="exact")
+    torch.cuda.synchronize()
+    _check_mx_exact(f32(c), qa, sa, fa, qb, sb, fb, out)
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e5m2")])
+def test_gemm_mx_exact_window_edges_zero_blocks_and_nan_rows(fa, fb):
+    """Rows whose block exponents span exactly 47 (the window's edge) stay
+    within the bound; all-zero blocks (code 127) next to small blocks inside the
+    window are harmless; a row of A and a row of B spanning 48 are reported as
+    NaN rows / columns, every other output within the bound."""
+    M, N, K = 260, 300, 512
+    rng = np.random.default_rng(47)
+    qa, sa = _rand_mx(rng, M, K, fa, 110, 140)
+    qb, sb = _rand_mx(rng, N, K, fb, 110, 140)
+    sa[5, :] = 120
+    sa[5, 3], sa[5, 9] = 160, 113                # span 47 exactly
+    sb[7, :] = 130
+    sb[7, 0], sb[7, 15] = 90, 137                # span 47
+    qa[11, 64:96] = 0
+    sa[11, :] = 100
+    sa[11, 2] = 127                               # an all-zero block with code 127, others 27 below
+    sa[200, 0], sa[200, 1] = 170, 122            # span 48: outside
+    sb[250, 4], sb[250, 5] = 100, 148            # span 48: outside
+    dev = device()
+    c = torch.empty((M, N), dtype=torch.float32, device=dev)
+    fm.fp8_gemm_mx(torch.from_numpy(qa).to(dev), fa, _dev_scales(sa, dev), torch.from_numpy(qb).to(dev), fb,
+                   _dev_scales(sb, dev), c, accum="exact")
+    torch.cuda.synchronize()
+    _check_mx_exact(f32(c), qa, sa, fa, qb, sb, fb, "f32", nan_rows=[200], nan_cols=[250])
