@@ -36,7 +36,9 @@ can pin the others:
 
 Parity status: pinned (exhaustive round trip of all 256 codes per format,
 encoder agreement over every fp32 bit pattern in each format's active band,
-brute force on samples, the pages' worked numbers).
+brute force on samples, the pages' worked numbers; ``encode`` equals the
+value-based C encoder of codec_ref.c on all 2^32 fp32 bit patterns of both
+formats, tests/test_oracle_codec_exhaustive.py).
 """
 
 from __future__ import annotations

@@ -42,7 +42,10 @@ Definitions used here
                              sum_{k in kb} dec(a[m,k]) dec(b_g[n,k]).
 
 Parity status: requant_bracket is pinned by hand-computed codes (exact
-values, a round-to-even midpoint, saturation) in tests/test_oracle_gemm.py.
+values, a round-to-even midpoint, saturation) in tests/test_oracle_gemm.py;
+grouped_abs_bound by an exact Fraction evaluation of its definition (an empty
+expert, partial weight and K blocks, per-row / per-block / negative scales)
+and by its identity with 1e-5 times the grouped sum of magnitudes.
 The sum is pinned (exact integer dot products on small
 matrices and on sampled elements; one-hot, permutation, all-zero and
 all-max operands with closed-form results).  The fp32 accumulation ORDER of
