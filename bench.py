@@ -35,10 +35,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "FP8 GEMM TFLOPS (% MFMA peak) at 8192x4096x16384; cast+amax HBM GB/s"
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA, published
-PEAK_FP16_TFLOPS = 2500.0     # MI355X dense FP16/BF16 MFMA, published
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense BF16/FP16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 # Matrix-core peak of the instruction each accumulation mode runs on.
-PEAK_BY_ACCUM = {"exact": PEAK_FP16_TFLOPS, "mfma_fp8": PEAK_FP8_TFLOPS}
+PEAK_BY_ACCUM = {"exact": PEAK_BF16_TFLOPS, "mfma_fp8": PEAK_FP8_TFLOPS}
 
 # HBM traffic per launch of the FC1 GEMM from two counter runs (FETCH_SIZE, WRITE_SIZE), each scaled by what
 # the same counter reads for a 256 MiB device copy (profiles/gemm_fc1_8192x16384x4096_hbm_traffic.md).  Valid
@@ -487,7 +487,7 @@ def mx_bench(torch, fm, iters=20):
     res = {"us": us,
            "gemm_exact_tflops": flops / us["gemm_exact"] / 1e6,
            "gemm_exact_frac_of_fp8_peak": flops / us["gemm_exact"] / 1e6 / PEAK_FP8_TFLOPS,
-           "gemm_exact_frac_of_bf16_peak": flops / us["gemm_exact"] / 1e6 / PEAK_FP16_TFLOPS,
+           "gemm_exact_frac_of_bf16_peak": flops / us["gemm_exact"] / 1e6 / PEAK_BF16_TFLOPS,
            "gemm_mfma_fp8_tflops": flops / us["gemm_mfma_fp8"] / 1e6,
            "gemm_mfma_fp8_frac_of_fp8_peak": flops / us["gemm_mfma_fp8"] / 1e6 / PEAK_FP8_TFLOPS,
            "quantize_x_gbs": M * K * (2 + 1 + 1 / 32) / us["quantize_x"] / 1e3,
@@ -743,7 +743,7 @@ def main():
                      "frac": round(head["gemm_tflops"] / PEAK_FP8_TFLOPS, 4),
                      "traffic": gemm_traffic(args.accum),
                      "kernel": "gemm_kernel (%s accumulation: %s matrix cores)"
-                               % (args.accum, "fp16" if args.accum == "exact" else "fp8"),
+                               % (args.accum, "bf16" if args.accum == "exact" else "fp8"),
                      "instruction_peak": PEAK_BY_ACCUM[args.accum],
                      "frac_of_instruction_peak": round(head["gemm_tflops"] / PEAK_BY_ACCUM[args.accum], 4)},
         "cpu_baseline": cpu,

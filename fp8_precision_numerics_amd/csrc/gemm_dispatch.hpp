@@ -19,7 +19,7 @@ inline hipError_t gemm_run(const uint8_t* A, const uint8_t* B, int64_t M, int64_
   return hipGetLastError();
 }
 
-// 256x256 tiles.  fp16 path: 4 wavefronts (one per SIMD, 128x128 each, the
+// 256x256 tiles.  bf16 paths: 4 wavefronts (one per SIMD, 128x128 each, the
 // accumulators in the AGPR half of the register file).  FP8 path: 8
 // wavefronts (two per SIMD, 64x128 each) to hide more latency.  Small
 // problems: 128x128 tiles of four 64x64 wavefronts.  BT: B stored [K x N]

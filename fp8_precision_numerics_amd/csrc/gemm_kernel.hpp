@@ -7,9 +7,9 @@
 //     the end of the step, so their latency overlaps the step;
 //   * FP8 path: the wave's A fragments for step t are in registers; its B
 //     fragments are read one 16-row block ahead (bf[(j+1)&1] while the MFMAs
-//     of block j run).  fp16 path: the raw FP8 fragments of the step are read
+//     of block j run).  bf16 paths: the raw FP8 fragments of the step are read
 //     one 16-byte granule ahead of the sub-steps that use them and widened to
-//     fp16 per 16-deep sub-step;
+//     bf16 per 16-deep sub-step;
 //   * at the end of the step: wait for this lane's loads, barrier, then read
 //     the fragments of step t+1.
 //
@@ -527,7 +527,7 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
     int tiles_m, int tiles_n, int group_m, RequantArgs rq, MxScales mxs) {
   constexpr int NW = WM * WN, NT = 64 * NW;
   constexpr int WTM = BM / WM, WTN = BN / WN;
-  // Output block of one matrix-core instruction: 16x16 (FP8 paths), 32x32 (fp16 path).
+  // Output block of one matrix-core instruction: 16x16 (FP8 paths), 32x32 (bf16 paths).
   constexpr bool MX = MODE == kAccumMx;
   constexpr bool MXE = MODE == kAccumMxExact;
   constexpr bool MXS = MX || MXE;  // stages carry the step's E8M0 block scales
@@ -560,8 +560,8 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
   auto stage_ragged = [&](int kt, int stage) { slabs.ragged(smem + stage * STAGE, kt, t); };
 
   // Fragment reads.  FP8 path (16x16x128): lane l takes row l & 15 of a
-  // 16-row block and the 32-byte K slice l >> 4 (granules 2h, 2h+1).  fp16
-  // path (32x32x16, eight K sub-steps of 16): lane l takes row l & 31 of a
+  // 16-row block and the 32-byte K slice l >> 4 (granules 2h, 2h+1).  bf16
+  // paths (32x32x16, eight K sub-steps of 16): lane l takes row l & 31 of a
   // 32-row block and the 64-byte half l >> 5 of the K step (granules 4h..4h+3);
   // sub-step s uses bytes [8s, 8s+8) of it, for both operands alike.  Block
   // starts are multiples of 16 rows, so the swizzle of a lane's row is fixed.
@@ -763,8 +763,8 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
       }
     });
   } else {
-    // fp16 path (kAccumExact) or bf16 path with block scales (kAccumMxExact)
-    using H8 = std::conditional_t<MXE, v8bf, v8h>;
+    // bf16 paths: per-tensor (kAccumExact) or with block scales (kAccumMxExact)
+    using H8 = v8bf;
     v16f acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -816,16 +816,13 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
       }
     };
     auto widen_a = [&](uint32_t w0, uint32_t w1, int i) -> H8 {
-      if constexpr (MXE) return widen8_scaled_bf16<FA>(w0, w1, fa[i]);
-      else return widen8<FA>(w0, w1);
+      return widen8_scaled_bf16<FA>(w0, w1, MXE ? fa[i] : 1.0f);
     };
     auto widen_b = [&](uint32_t w0, uint32_t w1, int j) -> H8 {
-      if constexpr (MXE) return widen8_scaled_bf16<FB>(w0, w1, fb[j]);
-      else return widen8<FB>(w0, w1);
+      return widen8_scaled_bf16<FB>(w0, w1, MXE ? fb[j] : 1.0f);
     };
     auto mfma = [&](const H8& b, const H8& a, const v16f& c) {
-      if constexpr (MXE) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
-      else return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
     };
     // Raw FP8 fragments of the whole step: 4 granules (64 bytes) per block.
     // Only granule 0 is read right after the barrier; granule c + 1 is read

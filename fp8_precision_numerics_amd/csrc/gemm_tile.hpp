@@ -3,17 +3,21 @@
 // Two ways to contract FP8 operands on gfx950 (selected per call):
 //
 // * kAccumExact — every product exact, sums in fp32.  The FP8 codes are
-//   widened in registers to fp16 (exact for both E4M3 and E5M2, subnormals
-//   included: V_CVT_SCALEF32_PK_F16_FP8/BF8 with scale 1) and contracted with
-//   V_MFMA_F32_32X32X16_F16 (no loss was found in its fp32 sums).  This is
-//   "GEMM in FP8, FP32 accumulation" in the sense of "4.2 Hopper I — Transformer
-//   Engine·FP8" §4.2.4: the result meets 1e-5·Σ|ab| for every input.
+//   widened in registers to bf16 (exact for both E4M3 and E5M2, subnormals
+//   included: V_CVT_SCALEF32_PK_BF16_FP8/BF8 with scale 1; bf16 keeps 8
+//   significant bits and fp32's exponent range) and contracted with
+//   V_MFMA_F32_32X32X16_BF16, whose products of such values are exact and whose
+//   sums are fp32 (no loss was found).  This is "GEMM in FP8, FP32
+//   accumulation" in the sense of "4.2 Hopper I — Transformer Engine·FP8"
+//   §4.2.4: the result meets 1e-5·Σ|ab| for every input.  (The fp16
+//   instruction, fed fp16-widened codes, returns the same bits; the bf16 one
+//   measured 1-1.5 % faster on MI355X.)
 //
 // * kAccumMfma8 — the native FP8 matrix-core instruction
 //   V_MFMA_F32_16X16X128_F8F6F4.  Measured on MI355X: it forms dot products of
 //   8 consecutive K terms in fixed point whose last bit lies 13 bits below
 //   the largest product of the 8, truncating the rest toward zero, and adds
-//   those partials in fp32.  Twice the rate of the fp16 path; the per-group
+//   those partials in fp32.  Twice the rate of the bf16 path; the per-group
 //   truncation (at most 8·2^-13 of the group's largest product) is its
 //   accuracy price.
 //
@@ -25,7 +29,7 @@
 // Unscaled, the kernels simply give lane group h the 32-byte slice h; scaled,
 // they give it the 16-byte pieces h and h + 4, so the hardware's K blocks are
 // the operand's.  32x32x16
-// (fp16 path): lane l supplies row l % 32 and the 64-byte half l / 32 of the
+// (bf16 paths): lane l supplies row l % 32 and the 64-byte half l / 32 of the
 // step, of which sub-step s (16 deep) takes bytes [8s, 8s+8).  Any assignment
 // of K values to (lane, register) slots works as long as both operands use the
 // same one.  The kernels feed the B tile (rows = n) as the instruction's first
@@ -51,15 +55,13 @@ constexpr int kBK = 128;  // K bytes per main-loop step
 // kAccumMx: the FP8 instruction with a power-of-two (E8M0) scale per 32-deep K
 // block of each operand row (MXFP8), applied by the instruction itself.
 // kAccumMxExact: MXFP8 operands with every product exact and fp32 sums: the
-// codes are widened to bf16 with the block's power of two relative to the
-// row's largest block exponent folded into the conversion (exact: bf16 keeps
-// 8 significant bits and fp32's exponent range), contracted with
-// V_MFMA_F32_32X32X16_BF16, and the two rows' reference powers of two are
-// applied in the epilogue.
+// codes are widened to bf16 as in kAccumExact but with the block's power of
+// two relative to the row's largest block exponent folded into the conversion
+// (still exact: the value keeps at most 4 significant bits inside bf16's
+// exponent range), contracted the same way, and the two rows' reference powers
+// of two are applied in the epilogue.
 enum : int { kAccumExact = 0, kAccumMfma8 = 1, kAccumMx = 2, kAccumMxExact = 3 };
 
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ int lds_swz(int row) { return (row & 6) | ((row >> 3) & 1); }
@@ -99,28 +101,11 @@ __device__ __forceinline__ v4f mfma_fp8_scaled(const v8i& first, const v8i& seco
   }
 }
 
-// Eight FP8 codes (bytes of w0 then w1) widened exactly to fp16.
-template <int F>
-__device__ __forceinline__ v8h widen8(uint32_t w0, uint32_t w1) {
-  v2h a, b, c, d;
-  if constexpr (F == kE4M3) {
-    a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
-    b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
-    c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
-    d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
-  } else {
-    a = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w0, 1.0f, false);
-    b = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w0, 1.0f, true);
-    c = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w1, 1.0f, false);
-    d = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w1, 1.0f, true);
-  }
-  return (v8h){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-// Eight FP8 codes (bytes of w0 then w1) times `scale` (a power of two),
-// converted to bf16.  Measured on MI355X: exact for every code of both formats
-// at every power of two from 2^-90 to 2^90 (the product has at most 4
-// significant bits and stays inside bf16's normal range there).
+// Eight FP8 codes (bytes of w0 then w1) times `scale` (a power of two; 1 for
+// the per-tensor path), converted to bf16.  Measured on MI355X: exact for
+// every code of both formats at every power of two from 2^-90 to 2^90 (the
+// product has at most 4 significant bits and stays inside bf16's normal range
+// there); Inf and NaN codes stay Inf and NaN.
 template <int F>
 __device__ __forceinline__ v8bf widen8_scaled_bf16(uint32_t w0, uint32_t w1, float scale) {
   v2bf a, b, c, d;

@@ -26,7 +26,7 @@
 //   the dense kernel's wave tile (64x128, A fragments resident, B streamed) in
 //   128x512 workgroup tiles: 128 rows because token counts come in multiples of
 //   128, 512 columns so that each wave's 128 columns meet one weight block.
-// * exact mode: the 16-deep fp16 instructions build P over eight sub-steps, so
+// * exact mode: the 16-deep bf16 instructions build P over eight sub-steps, so
 //   P and the accumulator are both live; 128x128 tiles of four 64x64 waves,
 //   two workgroups per CU.
 #include "gemm_kernel.hpp"
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(64 * WM* WN) void grouped_fp8_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Exact mode (FP8 widened to fp16, 32x32x16 instructions).
+// Exact mode (FP8 widened to bf16, 32x32x16 instructions).
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WM, int WN, int OUT>
 __global__ __launch_bounds__(64 * WM* WN) void grouped_exact_kernel(
@@ -294,19 +294,19 @@ __global__ __launch_bounds__(64 * WM* WN) void grouped_exact_kernel(
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      v8h bh[FN];
+      v8bf bh[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const uint4 g = br[j][s >> 1];
-        bh[j] = (s & 1) ? widen8<kE4M3>(g.z, g.w) : widen8<kE4M3>(g.x, g.y);
+        bh[j] = widen8_scaled_bf16<kE4M3>((s & 1) ? g.z : g.x, (s & 1) ? g.w : g.y, 1.0f);
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const uint4 g = ar[i][s >> 1];
-        const v8h ah = (s & 1) ? widen8<kE4M3>(g.z, g.w) : widen8<kE4M3>(g.x, g.y);
+        const v8bf ah = widen8_scaled_bf16<kE4M3>((s & 1) ? g.z : g.x, (s & 1) ? g.w : g.y, 1.0f);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bh[j], ah, part[i][j], 0, 0, 0);
+          part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[j], ah, part[i][j], 0, 0, 0);
       }
     }
     // Promotion of this 128-deep partial with its block scales.

@@ -125,8 +125,8 @@ def test_permutation_selects_columns_exactly(fa, fb, accum):
     of its format; A holds every finite code of its format in every row
     (shifted per row).  Each output is one exact product, so C must equal
     dec(A[m, perm[n]]) * dec(b_n) * sinv_a bit for bit: FP8 subnormals of
-    either operand (E5M2 0x01-0x03 become fp16 subnormals in the exact mode)
-    must survive the contraction unflushed."""
+    either operand (E5M2 0x01-0x03, E4M3 0x01-0x07) must survive the
+    contraction unflushed."""
     rng = np.random.default_rng(4)
     M, K = 200, 256
     codes_a = all_finite_codes(fa)
@@ -191,13 +191,13 @@ def test_b_trans_full_fc1_weight_layout():
 
 @pytest.mark.parametrize("fa", ["e4m3", "e5m2"])
 def test_fp8_matrix_cores_miss_the_method_bound_where_exact_mode_meets_it(fa):
-    """Why the headline GEMM contracts on the fp16 matrix cores.  Every run of 8
+    """Why the headline GEMM contracts on the bf16 matrix cores.  Every run of 8
     consecutive K products holds one product 448*448 (E4M3) or 57344*448 (E5M2
     times E4M3) and seven products 2^-10 of it.  The native FP8 instruction sums
     a run in fixed point 13 bits below its largest product, so each small
     product (binary 1100 0100 times a power of two, 4 bits below that grid) is
     cut by 4/196 of itself: the result misses 1e-5 * sum|ab| by an order of
-    magnitude.  The exact mode (FP8 widened to fp16, fp32 sums) returns the
+    magnitude.  The exact mode (FP8 widened to bf16, fp32 sums) returns the
     exact sum, which is representable here."""
     K = 256
     M = N = 64

@@ -58,3 +58,54 @@ def test_graph_replays_match_eager_delayed_scaling(fused):
         assert torch.equal(q_graph, q_eager)
         # unrelated eager work on the stream between replays
         torch.zeros(1 << 20, device=dev).add_(1.0).sum().item()
+
+
+def test_graph_replays_match_eager_linear_forward_step():
+    """The forward step of a linear layer as the benchmark replays it: the cast
+    of X, the cast-transpose of W (each with its history step) and the GEMM on
+    the codes, captured once per input set and replayed alternately.  Every
+    replay's codes, states and output must equal the same steps run eagerly."""
+    dev = device()
+    rng = np.random.default_rng(78)
+    M, K, N = 384, 640, 528           # the cast-transpose wants multiples of 16
+    sets = [(torch.from_numpy((rng.standard_normal((M, K)) * 2.0 ** j).astype(np.float32)).to(dev).to(torch.bfloat16),
+             torch.from_numpy((rng.standard_normal((K, N)) * 0.02 * 3.0 ** j).astype(np.float32)).to(dev).to(torch.bfloat16))
+            for j in range(2)]
+
+    def make():
+        return {"sx": fm.DelayedScalingState("e4m3", 16, device=dev), "sw": fm.DelayedScalingState("e4m3", 16, device=dev),
+                "qx": torch.empty((M, K), dtype=torch.uint8, device=dev),
+                "qw": torch.empty((N, K), dtype=torch.uint8, device=dev),
+                "c": torch.empty((M, N), dtype=torch.bfloat16, device=dev)}
+
+    def step(s, x, w):
+        s["sx"].quantize_update(x, q=s["qx"])
+        s["sw"].quantize_update(w, q_t=s["qw"])
+        fm.fp8_gemm(s["qx"], "e4m3", s["qw"], "e4m3", s["sx"].scale_inv_used, s["sw"].scale_inv_used, s["c"])
+
+    g, e = make(), make()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(make(), *sets[0])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for x, w in sets:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            step(g, x, w)
+        graphs.append(gr)
+    for replay, j in enumerate([0, 1, 0, 1]):
+        announce(f"linear forward step graph replay {replay} (input set {j})")
+        graphs[j].replay()
+        step(e, *sets[j])
+        torch.cuda.synchronize()
+        for k in ("sx", "sw"):
+            a, b = _state_arrays(g[k]), _state_arrays(e[k])
+            for f in a:
+                assert np.array_equal(a[f].view(np.uint8), b[f].view(np.uint8)), (replay, k, f)
+        for k in ("qx", "qw"):
+            assert torch.equal(g[k], e[k]), (replay, k)
+        assert torch.equal(g["c"].view(torch.int16), e["c"].view(torch.int16)), replay
+        torch.zeros(1 << 20, device=dev).add_(1.0).sum().item()
