@@ -44,9 +44,9 @@ PEAK_BY_ACCUM = {"exact": PEAK_BF16_TFLOPS, "mfma_fp8": PEAK_FP8_TFLOPS}
 # the same counter reads for a 256 MiB device copy (profiles/gemm_fc1_8192x16384x4096_hbm_traffic.md).  Valid
 # only for the kernel sources they were taken on: GEMM_SOURCES hashed in order must give GEMM_TRAFFIC_SHA256.
 GEMM_SOURCES = ("gemm.hip", "gemm_dispatch.hpp", "gemm_kernel.hpp", "gemm_tile.hpp", "device_common.hpp")
-GEMM_TRAFFIC_SHA256 = "091a2745dea833b8085cf8c641d4a4d3dc3eb286190ea8bd5c8a1181a4088a3d"
-GEMM_TRAFFIC = {"exact": {"read_bytes": 1208342036, "write_bytes": 268682048},
-                "mfma_fp8": {"read_bytes": 1208542119, "write_bytes": 269108757}}
+GEMM_TRAFFIC_SHA256 = "6e01e888e9eeaacd9c5b5147511c67687cdfd6e5a47da86a961aea03167b69af"
+GEMM_TRAFFIC = {"exact": {"read_bytes": 1208363031, "write_bytes": 268577664},
+                "mfma_fp8": {"read_bytes": 1208681569, "write_bytes": 268889429}}
 
 
 def gemm_traffic(accum):
