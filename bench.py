@@ -71,7 +71,7 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--quick", action="store_true", help="headline step only (no extras, no CPU baseline)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--with-stream", action="store_true",
@@ -134,41 +134,58 @@ def headline(torch, fm, args):
     qx = torch.empty((M, K), dtype=torch.uint8, device=dev)
     qwT = torch.empty((N, K), dtype=torch.uint8, device=dev)
     c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    t_cx, t_cw, t_gemm = EventTimer(torch), EventTimer(torch), EventTimer(torch)
+    t_gemm = EventTimer(torch)
 
     # One delayed-scaling step per tensor per call (cast, then the history step
     # that sets the next step's scale); the GEMM takes the inverse scales the
     # casts used.
-    def step(i, timed):
-        Xi, Wi = Xs[i % NSETS], Ws[i % NSETS]
-        if timed:
-            with t_cx:
-                stX.quantize_update(Xi, q=qx)
-            with t_cw:
-                stW.quantize_update(Wi, q_t=qwT)
-            with t_gemm:
-                fm.fp8_gemm(qx, "e4m3", qwT, "e4m3", stX.scale_inv_used, stW.scale_inv_used, c, accum=args.accum)
-        else:
-            stX.quantize_update(Xi, q=qx)
-            stW.quantize_update(Wi, q_t=qwT)
-            fm.fp8_gemm(qx, "e4m3", qwT, "e4m3", stX.scale_inv_used, stW.scale_inv_used, c, accum=args.accum)
+    def casts(i):
+        stX.quantize_update(Xs[i % NSETS], q=qx)
+        stW.quantize_update(Ws[i % NSETS], q_t=qwT)
+
+    def gemm():
+        fm.fp8_gemm(qx, "e4m3", qwT, "e4m3", stX.scale_inv_used, stW.scale_inv_used, c, accum=args.accum)
 
     for i in range(args.warmup):
-        step(i, False)
+        casts(i)
+        gemm()
     torch.cuda.synchronize()
+    # Timed region.  A timing event left in the stream idles the GPU for about
+    # 10 us where it sits (MI355X kernel trace: a gap at each event boundary,
+    # none between the launches of the untimed steps, whatever the event's
+    # release scope), so the GEMM is bracketed by events on every other step
+    # only: its mean duration over those launches, measured live on its stream,
+    # gives the roofline, and the steps between keep the launches back to back.
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(args.steps):
-        step(args.warmup + i, True)
+        casts(args.warmup + i)
+        if i % 2 == 0:
+            with t_gemm:
+                gemm()
+        else:
+            gemm()
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     flops = 2.0 * M * N * K
     gemm_ms = statistics.mean(t_gemm.ms())
+    # The casts, each between events, in the same steps run after the timed
+    # region: the per-call cost of each (its events' gaps included).
+    t_cx, t_cw = EventTimer(torch), EventTimer(torch)
+    for i in range(args.steps):
+        j = args.warmup + args.steps + i
+        with t_cx:
+            stX.quantize_update(Xs[j % NSETS], q=qx)
+        with t_cw:
+            stW.quantize_update(Ws[j % NSETS], q_t=qwT)
+        gemm()
+    torch.cuda.synchronize()
     cx_ms, cw_ms = statistics.mean(t_cx.ms()), statistics.mean(t_cw.ms())
-    log(f"step {total_ms / args.steps:.3f} ms; gemm {gemm_ms * 1e3:.1f} us ({flops / gemm_ms / 1e9:.0f} TFLOP/s); "
-        f"cast X + history step {cx_ms * 1e3:.1f} us; cast-transpose W + history step {cw_ms * 1e3:.1f} us")
+    log(f"step {total_ms / args.steps:.3f} ms; gemm {gemm_ms * 1e3:.1f} us ({flops / gemm_ms / 1e9:.0f} TFLOP/s, "
+        f"{len(t_gemm.pairs)} of {args.steps} launches timed); cast X + history step {cx_ms * 1e3:.1f} us; "
+        f"cast-transpose W + history step {cw_ms * 1e3:.1f} us")
     # the same GEMM in the other accumulation mode, alone
     other = "mfma_fp8" if args.accum == "exact" else "exact"
     t_other = EventTimer(torch)
