@@ -12,7 +12,13 @@ inline hipError_t gemm_run(const uint8_t* A, const uint8_t* B, int64_t M, int64_
                            const float* sb, void* C, const RequantArgs& rq, hipStream_t st,
                            const MxScales& mxs = MxScales{nullptr, nullptr}) {
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-  const int group_m = 16;
+  // Bands of 4 tile-rows: with one 256x256 workgroup per CU, each XCD's 32
+  // resident tiles then form a 4 x 8 block, whose K steps fill the XCD's L2
+  // with 12 operand slabs instead of the 18 of a 16 x 2 block.  Measured on
+  // MI355X in steady state (after the clock has settled): 0.7-1.8 % faster
+  // for the exact kernel and 3.5 % for the FP8 one than bands of 16; bands of
+  // 8 and 2 in between.
+  const int group_m = 4;
   hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, FA, FB, OUT, MODE, BT>), dim3((unsigned)(tiles_m * tiles_n)),
                      dim3(64 * WM * WN), 0, st, A, B, (int)M, (int)N, (int)K, sa, sb, C, tiles_m, tiles_n, group_m,
                      rq, mxs);
