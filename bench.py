@@ -44,9 +44,9 @@ PEAK_BY_ACCUM = {"exact": PEAK_BF16_TFLOPS, "mfma_fp8": PEAK_FP8_TFLOPS}
 # the same counter reads for a 256 MiB device copy (profiles/gemm_fc1_8192x16384x4096_hbm_traffic.md).  Valid
 # only for the kernel sources they were taken on: GEMM_SOURCES hashed in order must give GEMM_TRAFFIC_SHA256.
 GEMM_SOURCES = ("gemm.hip", "gemm_dispatch.hpp", "gemm_kernel.hpp", "gemm_tile.hpp", "device_common.hpp")
-GEMM_TRAFFIC_SHA256 = "6e01e888e9eeaacd9c5b5147511c67687cdfd6e5a47da86a961aea03167b69af"
-GEMM_TRAFFIC = {"exact": {"read_bytes": 1208363031, "write_bytes": 268577664},
-                "mfma_fp8": {"read_bytes": 1208681569, "write_bytes": 268889429}}
+GEMM_TRAFFIC_SHA256 = "b73231fc860dbd45b6c4ccbe536619a487c43cee10cfe32fa0f466f2bca27a67"
+GEMM_TRAFFIC = {"exact": {"read_bytes": 806133328, "write_bytes": 268482505},
+                "mfma_fp8": {"read_bytes": 805657436, "write_bytes": 268811819}}
 
 
 def gemm_traffic(accum):
