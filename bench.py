@@ -63,6 +63,12 @@ def gemm_traffic(accum):
     return t["read_bytes"] + t["write_bytes"]
 
 
+def _percentiles(xs, ps):
+    """Nearest-rank percentiles of xs."""
+    s = sorted(xs)
+    return [s[min(len(s) - 1, max(0, int(round(p / 100 * len(s) + 0.5)) - 1))] for p in ps]
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -70,7 +76,7 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--quick", action="store_true", help="headline step only (no extras, no CPU baseline)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -207,6 +213,7 @@ def headline(torch, fm, args):
         "value": flops / (total_ms / args.steps) / 1e9,
         "gemm_ms": gemm_ms,
         "gemm_ms_median": statistics.median(t_gemm.ms()),
+        "gemm_us_p10_p50_p90": [round(float(x), 1) for x in _percentiles([v * 1e3 for v in t_gemm.ms()], (10, 50, 90))],
         "gemm_tflops": flops / gemm_ms / 1e9,
         "gemm_frac_of_fp8_peak": flops / gemm_ms / 1e9 / PEAK_FP8_TFLOPS,
         "cast_x_us": cx_ms * 1e3,

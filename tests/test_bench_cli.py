@@ -19,7 +19,7 @@ def test_defaults_are_one_gpu_and_bounded_steps():
         args = bench.parse()
     finally:
         sys.argv = old
-    assert args.gpus == 1 and 1 <= args.steps <= 100 and 0 <= args.warmup <= 20
+    assert args.gpus == 1 and 1 <= args.steps <= 100 and 0 <= args.warmup <= 100
     assert args.accum == "exact"
 
 
