@@ -61,10 +61,51 @@ __device__ __forceinline__ bool expert_tile(const int32_t* __restrict__ m_offset
   return false;
 }
 
+// Output tile (mt, tn) of workgroup `wg`.  GM == 0: consecutive workgroups
+// walk the N tiles of one M tile (the round-robin deal of workgroups to the 8
+// XCDs then gives each XCD a fixed set of columns).  GM > 0: each XCD takes a
+// contiguous range of the real tiles (the M tiles the experts' rows fill, not
+// the grid's upper bound, so the padding tiles do not pile up on one XCD),
+// walked in bands of GM M tiles, so the workgroups resident on one XCD form a
+// compact block of tiles.  False for a workgroup with no tile.  The grid must
+// be a multiple of 8 workgroups at least as large as the tile count.
+template <int BM, int GM>
+__device__ __forceinline__ bool grouped_tile(const int32_t* __restrict__ m_offsets, int G, int total_m, int tiles_n,
+                                             int wg, int* mt, int* tn) {
+  if constexpr (GM == 0) {
+    *tn = wg % tiles_n;
+    *mt = wg / tiles_n;
+    return true;
+  } else {
+    int real_m = 0, prev = 0;
+    for (int g = 0; g < G; ++g) {
+      int lo = m_offsets[g], hi = m_offsets[g + 1];
+      lo = lo < prev ? prev : (lo > total_m ? total_m : lo);
+      hi = hi < lo ? lo : (hi > total_m ? total_m : hi);
+      prev = hi;
+      real_m += (hi - lo + BM - 1) / BM;
+    }
+    const int total = real_m * tiles_n;
+    const int per_xcd = (total + 7) >> 3;
+    const int j = wg >> 3;
+    if (j >= per_xcd) return false;
+    const int pid = (wg & 7) * per_xcd + j;
+    if (pid >= total) return false;
+    const int in_group = GM * tiles_n;
+    const int gid = pid / in_group;
+    const int first_m = gid * GM;
+    const int gsize = (real_m - first_m) < GM ? (real_m - first_m) : GM;
+    const int local = pid - gid * in_group;
+    *mt = first_m + local % gsize;
+    *tn = local / gsize;
+    return true;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // FP8 matrix-core mode.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int OUT>
+template <int BM, int BN, int WM, int WN, int OUT, int GM = 0>
 __global__ __launch_bounds__(64 * WM* WN) void grouped_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sinv_a, const uint8_t* __restrict__ B,
     const float* __restrict__ sinv_b, const int32_t* __restrict__ m_offsets, int G, int total_m,
@@ -77,9 +118,8 @@ __global__ __launch_bounds__(64 * WM* WN) void grouped_fp8_kernel(
   constexpr int STAGE = (BM + BN) * kBK;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
-  // Consecutive workgroups walk the N tiles of one M tile; the round-robin
-  // deal of workgroups to XCDs then gives each XCD a fixed set of columns.
-  const int tn = blockIdx.x % tiles_n, mt = blockIdx.x / tiles_n;
+  int mt, tn;
+  if (!grouped_tile<BM, GM>(m_offsets, G, total_m, tiles_n, blockIdx.x, &mt, &tn)) return;  // uniform exit
   int gidx;
   int64_t row0, row_end;
   if (!expert_tile<BM>(m_offsets, G, total_m, mt, &gidx, &row0, &row_end)) return;  // uniform exit
@@ -210,7 +250,9 @@ __global__ __launch_bounds__(64 * WM* WN) void grouped_exact_kernel(
   constexpr int STAGE = (BM + BN) * kBK;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
-  const int tn = blockIdx.x % tiles_n, mt = blockIdx.x / tiles_n;
+  // The plain order (grouped_tile<BM, 0>): the banded ones measured 1 % slower here.
+  int mt, tn;
+  if (!grouped_tile<BM, 0>(m_offsets, G, total_m, tiles_n, blockIdx.x, &mt, &tn)) return;  // uniform exit
   int gidx;
   int64_t row0, row_end;
   if (!expert_tile<BM>(m_offsets, G, total_m, mt, &gidx, &row0, &row_end)) return;  // uniform exit
@@ -345,12 +387,14 @@ __global__ __launch_bounds__(64 * WM* WN) void grouped_exact_kernel(
 }
 
 // Grid: N tiles times an upper bound on the M tiles over any split of total_m
-// rows into G experts (each expert adds at most one partial tile).
+// rows into G experts (each expert adds at most one partial tile), rounded up
+// to a multiple of the 8 XCDs (grouped_tile); workgroups past the real tiles
+// exit at once.
 template <int BM, int BN>
 dim3 grouped_grid(int64_t total_m, int G, int64_t N, int* tiles_n) {
   *tiles_n = (int)((N + BN - 1) / BN);
   const int64_t tiles_m = (total_m + BM - 1) / BM + G;
-  return dim3((unsigned)(tiles_m * *tiles_n));
+  return dim3((unsigned)((tiles_m * *tiles_n + 7) / 8 * 8));
 }
 
 template <int BM, int BN, int WM, int WN, int OUT>
@@ -358,7 +402,10 @@ hipError_t run_fp8(const uint8_t* A, const float* sa, const uint8_t* B, const fl
                    int G, int64_t total_m, int64_t N, int64_t K, void* C, hipStream_t st) {
   int tiles_n;
   const dim3 grid = grouped_grid<BM, BN>(total_m, G, N, &tiles_n);
-  hipLaunchKernelGGL((grouped_fp8_kernel<BM, BN, WM, WN, OUT>), grid, dim3(64 * WM * WN), 0, st, A, sa, B, sb,
+  // Bands of 4 M tiles (MoE shape, MI355X, identical output): 5 % faster than
+  // the plain order launched back to back, level with it (0.4 %) right after
+  // the block quantisers and the exact kernel.
+  hipLaunchKernelGGL((grouped_fp8_kernel<BM, BN, WM, WN, OUT, 4>), grid, dim3(64 * WM * WN), 0, st, A, sa, B, sb,
                      offs, G, (int)total_m, (int)N, (int)K, C, tiles_n);
   return hipGetLastError();
 }
