@@ -589,14 +589,14 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
   // unscaled c and the saturation count cover only outputs inside M x N;
   // `mask` (a std::integral_constant) is false for tiles wholly inside C,
   // which skips the bounds tests.  Saturation is |p| > max as a float
-  // comparison (false for NaN, true for Inf), counted by a wave ballot: FP8
-  // tiles go out in a single pass, so every lane is active at every call.
+  // comparison (false for NaN, true for Inf), counted per lane and summed over
+  // the wave once, when the tile is done.
   // Common case (no NaN among the four scaled values, tested through their
   // sum, which an Inf - Inf also sends down the other path): the short
   // encoder and a float maximum of |c|.  Otherwise the full rule and
   // bit-pattern maxima (NaN above Inf).
   float rq_maxf = 0.0f;
-  uint32_t rq_max = 0, rq_sat_wave = 0;
+  uint32_t rq_max = 0, rq_sat_lane = 0;
   float rq_scale = 1.0f;
   if constexpr (OUT == kOutE4M3 || OUT == kOutE5M2) rq_scale = rq.out_scale[0];
   const int rows_left = (int)((M - m_base) < BM ? (M - m_base) : BM);
@@ -615,7 +615,7 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        rq_sat_wave += __builtin_popcountll(__builtin_amdgcn_ballot_w64(ok[e] && __builtin_fabsf(p[e]) > kMax));
+        rq_sat_lane += (ok[e] && __builtin_fabsf(p[e]) > kMax) ? 1u : 0u;
       const float t = (p[0] + p[1]) + (p[2] + p[3]);
       uint32_t codes;
       if (__builtin_expect(t == t, 1)) {
@@ -642,7 +642,7 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
   auto write_tile = [&](auto&& emit) {
     using TW = TileWriter<OUT, BM, BN, NT>;
     constexpr int PASS = pass_rows<BM>(2 * STAGE, TW::ROWB);
-    static_assert(PASS == BM || OUT == kF32 || OUT == kBF16, "FP8 tiles go out in one pass (ballot counts)");
+    static_assert(PASS == BM || OUT == kF32 || OUT == kBF16, "FP8 tiles go out in one pass");
     TW tw{smem, PASS};
 #pragma unroll 1
     for (int r0 = 0; r0 < BM; r0 += PASS) {
@@ -938,7 +938,7 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
   if constexpr (OUT == kOutE4M3 || OUT == kOutE5M2) {
     // |c| of the common path as bits (non-negative floats order as their bit patterns)
     const uint32_t mf = f2u(rq_maxf);
-    publish_requant_stats(mf > rq_max ? mf : rq_max, rq_sat_wave, rq_seen, rq, lane);
+    publish_requant_stats(mf > rq_max ? mf : rq_max, wave_sum_u32(rq_sat_lane), rq_seen, rq, lane);
   }
 }
 
