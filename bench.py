@@ -47,9 +47,9 @@ PEAK_BY_ACCUM = {"exact": PEAK_BF16_TFLOPS, "mfma_fp8": PEAK_FP8_TFLOPS}
 # the same counter reads for a 256 MiB device copy (profiles/gemm_fc1_8192x16384x4096_hbm_traffic.md).  Valid
 # only for the kernel sources they were taken on: GEMM_SOURCES hashed in order must give GEMM_TRAFFIC_SHA256.
 GEMM_SOURCES = ("gemm.hip", "gemm_dispatch.hpp", "gemm_kernel.hpp", "gemm_tile.hpp", "device_common.hpp")
-GEMM_TRAFFIC_SHA256 = "b73231fc860dbd45b6c4ccbe536619a487c43cee10cfe32fa0f466f2bca27a67"
-GEMM_TRAFFIC = {"exact": {"read_bytes": 806133328, "write_bytes": 268482505},
-                "mfma_fp8": {"read_bytes": 805657436, "write_bytes": 268811819}}
+GEMM_TRAFFIC_SHA256 = "cb94f503f2bc8e4331fdd24d7ba587aae52ae9fad0a9050d507833d9b444fc1e"
+GEMM_TRAFFIC = {"exact": {"read_bytes": 806160282, "write_bytes": 268496421},
+                "mfma_fp8": {"read_bytes": 805731237, "write_bytes": 268870075}}
 
 
 def gemm_traffic(accum):
