@@ -32,8 +32,6 @@ closed-form 448/amax and 57344/amax values.
 
 from __future__ import annotations
 
-import numpy as np
-
 from . import gemm, scaling
 
 __all__ = ["hybrid_linear_step"]
