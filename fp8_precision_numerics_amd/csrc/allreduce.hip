@@ -151,8 +151,7 @@ __global__ __launch_bounds__(256) void dequant_sum_kernel(const uint8_t* __restr
 
 template <int FMT, int OUT>
 hipError_t run_sum(const uint8_t* q, int R, int64_t n, int64_t stride, const float* si, void* out, hipStream_t st) {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int cus = persistent_groups(1);
   const int64_t nchunks = (n + kChunk - 1) / kChunk;
   int64_t blocks = (nchunks + 3) / 4;  // four waves per workgroup, one chunk each
   const int64_t cap = (int64_t)cus * 8;

@@ -21,6 +21,10 @@ struct HistoryArgs {
   float* sinv_used;  // receives *scale_inv as it was before the step (may be null)
 };
 
+// Workgroups of a grid with `per_cu` per compute unit of the current device
+// (the count is queried once per device; 256 compute units if the query fails).
+int persistent_groups(int per_cu);
+
 hipError_t launch_quantize(const void* x, int xtype, int64_t rows, int64_t cols, int fmt,
                            const float* scale, uint8_t* q, uint8_t* q_t, float* amax,
                            unsigned long long* sat, void* workspace, size_t workspace_bytes,

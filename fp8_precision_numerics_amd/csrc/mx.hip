@@ -173,8 +173,7 @@ __global__ __launch_bounds__(64 * kMxWaves) void quantize_mx_kernel(const void* 
 
 template <int FMT, int XT>
 hipError_t run_quantize_mx(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* scales, hipStream_t st) {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int cus = persistent_groups(1);
   const int64_t nbr = cols / 32, ld = mx_scale_ld(rows);
   const int64_t tiles_b = (nbr + kMxTileBlocks - 1) / kMxTileBlocks;
   const int64_t ntiles = (rows + kMxTileRows - 1) / kMxTileRows * tiles_b;

@@ -612,22 +612,28 @@ __global__ __launch_bounds__(kThreads) void quantize_block128_kernel(const void*
 // ---------------------------------------------------------------------------
 // Launch helpers (template dispatch).
 // ---------------------------------------------------------------------------
+}  // namespace
+
 // Workgroups of a persistent cast grid: `per_cu` per compute unit.  With
 // workspace partials each workgroup costs one 16-B slot.  Without them each
 // workgroup ends with device-scope atomics on single words, serialised across
 // the chip (about 10 ns each on MI355X), so that path keeps two per CU.
 int persistent_groups(int per_cu) {
-  static int cached[64] = {0};
+  // Compute units per device, queried once per device (relaxed atomics: every
+  // thread that races here stores the same value).
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256 * per_cu;
-  if (cached[dev] == 0) {
-    int cus = 0;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
-    cached[dev] = cus;
+    cached[dev].store(cus, std::memory_order_relaxed);
   }
-  return cached[dev] * per_cu;
+  return cus * per_cu;
 }
+
+namespace {
 
 // Workgroups of a cast grid with `partials` slots available (0: no partials,
 // atomics path).  The flat cast streams at the same rate with 2 or 4
