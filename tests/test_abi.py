@@ -136,11 +136,12 @@ def test_quantize_update_argument_errors(lib):
 
 def test_amax_update_argument_errors(lib):
     u = lib.fp8_amax_update
-    assert u(A16, 16, A16, A16, 5, A16, A16, None, None, None) == EFMT
-    assert u(None, 16, A16, A16, 0, A16, A16, None, None, None) == ENULL
-    assert u(A16, 16, A16, A16, 0, None, A16, None, None, None) == ENULL
-    assert u(A16, 0, A16, A16, 0, A16, A16, None, None, None) == ESHAPE
-    assert u(A16, 4097, A16, A16, 0, A16, A16, None, None, None) == ESHAPE
+    #        hist len  head amax fmt scale sinv status stream
+    assert u(A16, 16, A16, A16, 5, A16, A16, None, None) == EFMT
+    assert u(None, 16, A16, A16, 0, A16, A16, None, None) == ENULL
+    assert u(A16, 16, A16, A16, 0, None, A16, None, None) == ENULL
+    assert u(A16, 0, A16, A16, 0, A16, A16, None, None) == ESHAPE
+    assert u(A16, 4097, A16, A16, 0, A16, A16, None, None) == ESHAPE
 
 
 def test_gemm_argument_errors(lib):
