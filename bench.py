@@ -19,6 +19,10 @@ fine-grained MoE grouped GEMM, one GPU's parts of an E5M2 gradient all-reduce,
 MXFP8 (block-32 quantisation and the block-scaled GEMM) on the FC1 shape, and
 the vendor library's GEMMs on that shape; `cpu_baseline` times the CPU oracle on a
 bounded slice of the same step.
+
+Run order: the FC1 inputs and the CPU oracle (host work), the extras, the FC1
+GEMM in the other accumulation mode, then the FC1 steps (W warm-up, K timed),
+so that those start from the clock of a GPU under sustained matrix-core load.
 """
 
 from __future__ import annotations
