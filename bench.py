@@ -53,9 +53,9 @@ PEAK_BY_ACCUM = {"exact": PEAK_BF16_TFLOPS, "mfma_fp8": PEAK_FP8_TFLOPS}
 # the same counter reads for a 256 MiB device copy (profiles/gemm_fc1_8192x16384x4096_hbm_traffic.md).  Valid
 # only for the kernel sources they were taken on: GEMM_SOURCES hashed in order must give GEMM_TRAFFIC_SHA256.
 GEMM_SOURCES = ("gemm.hip", "gemm_dispatch.hpp", "gemm_kernel.hpp", "gemm_tile.hpp", "device_common.hpp")
-GEMM_TRAFFIC_SHA256 = "cb94f503f2bc8e4331fdd24d7ba587aae52ae9fad0a9050d507833d9b444fc1e"
-GEMM_TRAFFIC = {"exact": {"read_bytes": 806160282, "write_bytes": 268496421},
-                "mfma_fp8": {"read_bytes": 805731237, "write_bytes": 268870075}}
+GEMM_TRAFFIC_SHA256 = "8378fc2c46940d697a769763ea98beb8f4b2368d29ae1f8312cab35aa20fd5a4"
+GEMM_TRAFFIC = {"exact": {"read_bytes": 806237226, "write_bytes": 268657993},
+                "mfma_fp8": {"read_bytes": 805610545, "write_bytes": 268886224}}
 
 
 def gemm_traffic(accum):
