@@ -879,8 +879,16 @@ __global__ __launch_bounds__(64 * WM* WN) void gemm_kernel(
         load_fb(st, 0);
       }
       cvt_b(0, bb[0]);
+      // Raised wave priority for the first six sub-steps: with two waves per
+      // SIMD (8-wave tiles), one of them is favoured while both leave the
+      // step's barrier, so they stop issuing in lockstep.  FC1 on MI355X,
+      // identical output: 8 waves of 128x64 with this window 716.8 us, against
+      // 733.4 us for 4 waves of 128x128; windows of 5 or 7 sub-steps 720.3 and
+      // 721.4 us.  A lone wave per SIMD is unaffected.
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
+        if (s == 6) __builtin_amdgcn_s_setprio(0);
         if (s < kDmaGroups) dma(s);
         if ((s & 1) == 0 && (s >> 1) + 1 < 4) {
           read_granule(st, (s >> 1) + 1);

@@ -46,9 +46,9 @@ def slab_accesses(BM, BN, NW, rows_left_a, rows_left_b, K, kt):
     return out
 
 
-# (BM, BN, NW): dense exact 256x256 / 4 waves; dense FP8 and MX 256x256 / 8
-# waves; small problems 128x128 / 4 waves; grouped FP8 128x512 / 8 waves;
-# grouped exact 128x128 / 4 waves.
+# (BM, BN, NW): dense exact, FP8 and MXFP8 FP8-core 256x256 / 8 waves; MXFP8
+# exact 256x256 / 4 waves; small problems 128x128 / 4 waves; grouped FP8
+# 128x512 / 8 waves; grouped exact 128x128 / 4 waves.
 SHAPES = [(256, 256, 4), (256, 256, 8), (128, 128, 4), (128, 512, 8)]
 
 
