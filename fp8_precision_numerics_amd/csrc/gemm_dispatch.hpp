@@ -25,11 +25,11 @@ inline hipError_t gemm_run(const uint8_t* A, const uint8_t* B, int64_t M, int64_
   return hipGetLastError();
 }
 
-// 256x256 tiles.  Per-tensor exact path: 8 wavefronts (two per SIMD, 128x64
-// each, accumulators and operands in 246 VGPRs), 2-3 % faster on the FC1 GEMM
-// than 4 wavefronts of 128x128 (one per SIMD, accumulators in the AGPR half
-// of the register file) once the waves' priority window breaks their
-// lockstep (gemm_kernel.hpp); the MXFP8 exact path keeps the 4 wavefronts.
+// 256x256 tiles.  bf16 (exact) paths: 8 wavefronts (two per SIMD, 128x64
+// each, accumulators and operands in the VGPRs), faster on the FC1 GEMM than 4
+// wavefronts of 128x128 (one per SIMD, accumulators in the AGPR half of the
+// register file) once the waves' priority window breaks their lockstep
+// (gemm_kernel.hpp): per-tensor 2-3 %, MXFP8 8 % (812 against 881 us).
 // FP8 path: 8 wavefronts (two per SIMD, 64x128 each).  Small problems:
 // 128x128 tiles of four 64x64 wavefronts.  BT: B stored [K x N] (read through
 // the LDS transpose path), same tiles.
@@ -38,10 +38,8 @@ inline hipError_t gemm_dispatch_shape(const uint8_t* A, const uint8_t* B, int64_
                                       const float* sa, const float* sb, void* C, const RequantArgs& rq,
                                       hipStream_t st, const MxScales& mxs = MxScales{nullptr, nullptr}) {
   if (M >= 1024 && N >= 1024) {
-    if constexpr (MODE == kAccumExact)
+    if constexpr (MODE == kAccumExact || MODE == kAccumMxExact)
       return gemm_run<256, 256, 2, 4, FA, FB, OUT, MODE, BT>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
-    else if constexpr (MODE == kAccumMxExact)
-      return gemm_run<256, 256, 2, 2, FA, FB, OUT, MODE, BT>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
     else return gemm_run<256, 256, 4, 2, FA, FB, OUT, MODE, BT>(A, B, M, N, K, sa, sb, C, rq, st, mxs);
   }
   return gemm_run<128, 128, 2, 2, FA, FB, OUT, MODE, BT>(A, B, M, N, K, sa, sb, C, rq, st, mxs);

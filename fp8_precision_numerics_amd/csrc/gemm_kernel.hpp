@@ -428,7 +428,7 @@ struct MxScaleLoader {
 // silently inexact.  Output in LDS (refs): bytes [0, BM) and [BM, BM + BN) the
 // codes R of the A and B rows, floats at refs + 512: 2^(R - 127) or NaN.
 constexpr int kMxExactSpan = 47;
-constexpr int kMxRefBytes = 512 + 4 * 512 + 16 * 256;  // codes, factors, reduction scratch (256 threads)
+constexpr int kMxRefBytes = 512 + 4 * 512 + 16 * 512;  // codes, factors, reduction scratch (up to 512 threads)
 
 template <int BM, int BN, int NT>
 __device__ __forceinline__ void mx_row_refs(const MxScales& sx, int64_t m0, int64_t M, int64_t n0, int64_t N, int K,
@@ -467,7 +467,7 @@ __device__ __forceinline__ void mx_row_refs(const MxScales& sx, int64_t m0, int6
     }
   }
   // combine the LANES partial results of each dword through LDS
-  static_assert(NT * 16 <= 16 * 256, "reduction scratch");
+  static_assert(NT * 16 <= 16 * 512, "reduction scratch");
   uint32_t* part = reinterpret_cast<uint32_t*>(scratch);
   part[4 * t + 0] = __builtin_bit_cast(uint32_t, mx_lo);
   part[4 * t + 1] = __builtin_bit_cast(uint32_t, mx_hi);
