@@ -53,9 +53,9 @@ PEAK_BY_ACCUM = {"exact": PEAK_BF16_TFLOPS, "mfma_fp8": PEAK_FP8_TFLOPS}
 # the same counter reads for a 256 MiB device copy (profiles/gemm_fc1_8192x16384x4096_hbm_traffic.md).  Valid
 # only for the kernel sources they were taken on: GEMM_SOURCES hashed in order must give GEMM_TRAFFIC_SHA256.
 GEMM_SOURCES = ("gemm.hip", "gemm_dispatch.hpp", "gemm_kernel.hpp", "gemm_tile.hpp", "device_common.hpp")
-GEMM_TRAFFIC_SHA256 = "8378fc2c46940d697a769763ea98beb8f4b2368d29ae1f8312cab35aa20fd5a4"
-GEMM_TRAFFIC = {"exact": {"read_bytes": 806237226, "write_bytes": 268657993},
-                "mfma_fp8": {"read_bytes": 805610545, "write_bytes": 268886224}}
+GEMM_TRAFFIC_SHA256 = "2a8df5447029215bb2bf6d580f5b78871c0b499c58e48f090d1eb685663bfed5"
+GEMM_TRAFFIC = {"exact": {"read_bytes": 805546341, "write_bytes": 268523191},
+                "mfma_fp8": {"read_bytes": 805601577, "write_bytes": 268710760}}
 
 
 def gemm_traffic(accum):
