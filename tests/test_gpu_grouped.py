@@ -115,7 +115,8 @@ def _check_grouped(c, qa, sa, qb, sb, offs, out, rows=None, bound=None):
 @pytest.mark.parametrize("accum", ["exact", "mfma_fp8"])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("counts,K,N", [([64, 0, 200, 17], 272, 256), ([1], 128, 128), ([300, 129], 144, 260),
-                                        ([128] * 8, 512, 384), ([130, 0, 0, 1, 1000, 7, 256], 256, 1040)])
+                                        ([128] * 8, 512, 384), ([130, 0, 0, 1, 1000, 7, 256], 256, 1040),
+                                        ([200, 0, 77, 300], 1200, 384), ([129, 256], 2176, 256)])
 def test_grouped_small_within_bound(counts, K, N, out, accum):
     """Per-block-scaled N(0,1) activations and N(0,0.02) weights: the exact mode
     within the method's per-block bound, the FP8 matrix-core mode within the
