@@ -150,34 +150,36 @@ __global__ __launch_bounds__(64 * WM* WN) void grouped_fp8_kernel(
 
   // Block scales of the lane's output row in each A block and of the wave's
   // weight block, one step ahead: the values of step kt+1 are loaded while
-  // step kt runs.  The four lanes of a row (hh = 0..3) share its A scales:
-  // every fourth step each loads one of the next four steps' values (16 rows x
-  // 16 bytes per instruction), and each step takes its value from lane
-  // rr + 16*(kt % 4) with ds_bpermute.  In the three steps between, the same
-  // loads go out of range and read nothing, so the loop has no branch (a
-  // branch there made the register allocator spill).  Per-row loads every step
-  // cost 13 % (MoE shape, MI355X, identical output: 563.6 against 491.2 us).
-  // One buffer resource per A block covers the block's rows inside the expert;
-  // rows past it read as zero and are never stored.
+  // step kt runs.  The four lanes of a row (hh = 0..3, one K slice each) share
+  // its A scales: lane hh of block i holds step s + hh, for the last step
+  // s <= kt with s % 4 == i, and each step takes its value from lane
+  // rr + 16*((kt - i) % 4) with ds_bpermute.  Step kt refreshes only block
+  // kt % 4, from the one load issued during step kt - 1 (16 rows x 16 bytes).
+  // Loading every row's scale in every lane and step cost 13 % (MoE shape,
+  // MI355X, identical output: 563.6 against 491.2 us for all four blocks
+  // refreshed every fourth step, that form 1.8 % slower than this one); a
+  // branch around those loads made the register allocator spill.  One buffer
+  // resource covers the wave's rows inside the expert; rows past it read as
+  // zero and are never stored.
+  static_assert(FM == 4, "one A block refreshed per step of a 4-step group");
   const int64_t tile_rows = row_end - row0 < BM ? row_end - row0 : BM;
-  __amdgpu_buffer_rsrc_t rsa[FM];
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int64_t r = wm * WTM + i * 16;
-    int64_t bytes = (tile_rows > r ? tile_rows - r : 0) * nk * 4;  // < 2^31: kOutOfRange stays out of range
-    bytes = bytes < 0xFFFFFFFFll ? bytes : 0xFFFFFFFFll;
-    rsa[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sinv_a + (row0 + r) * nk), (short)0,
-                                               (int)(uint32_t)bytes, kBufferRsrcWord3);
-  }
+  const int64_t wave_rows = tile_rows - wm * WTM < 0 ? 0 : (tile_rows - wm * WTM < WTM ? tile_rows - wm * WTM : WTM);
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(sinv_a + (row0 + wm * WTM) * nk), (short)0, (int)(uint32_t)(wave_rows * nk * 4),
+      kBufferRsrcWord3);
+  auto steps_voff = [&](int blk, int first) {  // block blk, steps first .. first+3 (clamped)
+    int k = first + hh;
+    k = k < 0 ? 0 : (k < nk ? k : nk - 1);
+    return (uint32_t)(((blk * 16 + rr) * nk + k) * 4);
+  };
   const int nb = (int)((n_base + wn * WTN) >> 7);
   const float* sb_blk = sinv_b + ((int64_t)gidx * nbn + (nb < nbn ? nb : nbn - 1)) * nk;
-  float sa_q[FM] = {}, sa_t[FM], sb_n;
-  auto load_scales = [&](int kt) {
-    const int k = kt + hh < nk ? kt + hh : nk - 1;
-    const uint32_t voff = (kt & 3) == 0 ? (uint32_t)((rr * nk + k) * 4) : kOutOfRange;
+  float sa_q[FM], sa_next, sb_n;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      sa_t[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa[i], voff, 0, 0));
+  for (int i = 0; i < FM; ++i)
+    sa_q[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, steps_voff(i, i - 4), 0, 0));
+  auto load_scales = [&](int kt) {
+    sa_next = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, steps_voff(kt & 3, kt), 0, 0));
     sb_n = sb_blk[kt];
   };
   load_scales(0);
@@ -199,11 +201,10 @@ __global__ __launch_bounds__(64 * WM* WN) void grouped_fp8_kernel(
   auto compute = [&](const uint8_t* st, auto&& dma) {
     float s[FM];
     {
-      const int src = (rr + 16 * (kstep & 3)) * 4;
-      const bool fresh = (kstep & 3) == 0;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        sa_q[i] = fresh ? sa_t[i] : sa_q[i];
+        sa_q[i] = (kstep & 3) == i ? sa_next : sa_q[i];
+        const int src = (rr + 16 * ((kstep - i) & 3)) * 4;
         s[i] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, sa_q[i]))) * sb_n;
       }
     }
