@@ -225,3 +225,97 @@ def test_bt_transpose_reads_are_bank_conflict_free_and_select_the_right_values(B
             got = tr8(addr, lds)
             for lane, vals in got.items():
                 assert vals == [(krow0 + j, col0 + (lane & 15)) for j in range(8)]
+
+
+# ---------------------------------------------------------------------------
+# Grouped GEMM A block scales (fp8_precision_numerics_amd/csrc/grouped_gemm.hip).
+# sinv_a is [total_m][nk] fp32; a tile's buffer resource starts at its first row
+# and covers its rows inside the expert, so a load that passes the range check
+# stays inside them and rows past the expert read as zero.  Every offset is in
+# the VGPR operand (the scalar one is 0).
+
+GROUPED_TILE_ROWS = [1, 7, 16, 17, 63, 64, 65, 100, 127, 128]
+GROUPED_NK = [1, 2, 3, 7, 8, 9, 10, 16, 17, 56]
+
+
+@pytest.mark.parametrize("nk", GROUPED_NK)
+def test_grouped_exact_scale_chunks_reach_every_step(nk):
+    """Exact kernel (BM = 128, 4 waves): chunks of 8 steps in two LDS buffers of
+    [128 rows][8] fp32.  The prologue loads chunk 0 (each wave 4 loads of 8 rows);
+    step kt loads rows 16p .. 16p+15 of chunk kt/8 + 1 (p = kt % 8, waves 0 and 1)
+    when that chunk exists; the stage barrier publishes them.  Replays the loads
+    into an LDS model and checks that each step's read of row r gives
+    sinv_a[r][kt], and that every access that passes the range check lies inside
+    the tile's rows."""
+    BM, SCH, NW = 128, 8, 4
+    for tile_rows in GROUPED_TILE_ROWS:
+        nrec = min(tile_rows * nk * 4, U32_MAX)
+        lds = [[None] * (BM * SCH) for _ in range(2)]
+
+        def load(chunk, rb):
+            for lane in range(64):
+                sa_lane = ((lane >> 3) * nk + (lane & 7)) * 4
+                voff = sa_lane + (rb * nk + chunk * SCH) * 4
+                assert 0 <= voff < 2 ** 31
+                pos = rb * SCH + lane                       # M0 base + lane * 4 bytes
+                if voff + 4 > nrec:
+                    lds[chunk & 1][pos] = 0.0               # out of range: reads zero
+                    continue
+                row, k = divmod(voff // 4, nk)
+                assert row < tile_rows                      # inside the tile's rows
+                lds[chunk & 1][pos] = (row, k)
+
+        for w in range(NW):
+            for u in range(BM // 8 // NW):
+                load(0, 8 * (w + u * NW))
+        for kt in range(nk):
+            for r in range(BM):
+                v = lds[(kt // SCH) & 1][r * SCH + kt % SCH]
+                if r < tile_rows:
+                    assert v == (r, kt), (tile_rows, kt, r, v)
+            if (kt // SCH + 1) * SCH < nk:
+                for w in range(2):
+                    load(kt // SCH + 1, (kt % SCH) * 16 + 8 * w)
+
+
+@pytest.mark.parametrize("nk", GROUPED_NK)
+def test_grouped_fp8_staggered_scale_groups_reach_every_step(nk):
+    """FP8-core kernel (BM = 128, waves of 64 rows, FM = 4 blocks of 16 rows):
+    lane (rr, hh) of block i holds step s + hh for the last s <= kt with
+    s % 4 == i; step kt refreshes block kt % 4 with the load issued one step
+    earlier (clamped to the last step at the end) and reads block i from lane
+    rr + 16 * ((kt - i) % 4).  Checks that read against sinv_a[row][kt] for
+    every row inside the expert, and the bounds of every load."""
+    WTM, FM = 64, 4
+    for tile_rows in GROUPED_TILE_ROWS:
+        for wm in range(2):
+            wave_rows = max(0, min(tile_rows - wm * WTM, WTM))
+            nrec = wave_rows * nk * 4
+
+            def load(blk, first):
+                vals = {}
+                for lane in range(64):
+                    rr, hh = lane & 15, lane >> 4
+                    k = min(max(first + hh, 0), nk - 1)
+                    voff = ((blk * 16 + rr) * nk + k) * 4
+                    assert 0 <= voff < 2 ** 31
+                    if voff + 4 > nrec:
+                        vals[lane] = 0.0
+                        continue
+                    row, kk = divmod(voff // 4, nk)
+                    assert row < wave_rows and row == blk * 16 + rr and kk == k
+                    vals[lane] = (row, kk)
+                return vals
+
+            sa_q = [load(i, i - 4) for i in range(FM)]
+            sa_next = load(0, 0)                            # load_scales(0) in the prologue
+            for kt in range(nk):
+                sa_q[kt & 3] = sa_next
+                for i in range(FM):
+                    for rr in range(16):
+                        row = i * 16 + rr
+                        got = sa_q[i][rr + 16 * ((kt - i) & 3)]
+                        if row < wave_rows:
+                            assert got == (row, kt), (tile_rows, wm, kt, i, rr, got)
+                nxt = min(kt + 1, nk - 1)
+                sa_next = load(nxt & 3, nxt)
