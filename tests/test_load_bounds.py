@@ -1,8 +1,8 @@
 """Host-only replay of the GEMM kernels' buffer-load address arithmetic.
 
-The operand slabs and the MXFP8 block scales are fetched with buffer loads
-(fp8_precision_numerics_amd/csrc/gemm_kernel.hpp, SlabLoader and
-MxScaleLoader).  The hardware range check compares the per-lane VGPR offset
+The operand slabs, the MXFP8 block scales and the grouped GEMM's A block
+scales are fetched with buffer loads (fp8_precision_numerics_amd/csrc/
+gemm_kernel.hpp, SlabLoader and MxScaleLoader; grouped_gemm.hip).  The hardware range check compares the per-lane VGPR offset
 (plus the instruction offset, 0 here) with the resource's byte count; the
 scalar offset is added afterwards and is not checked.  A load whose VGPR
 offset passes the check therefore touches [base + voff + soff, +size): this
