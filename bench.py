@@ -701,7 +701,7 @@ def cpu_baseline(rows=8192, min_seconds=10.0, max_steps=3):
     it to a slice of X): delayed-scaled cast of `rows` rows of X, cast of the
     whole W, the dequantised GEMM of those rows (fp64 BLAS) and the history
     updates, repeated as consecutive steps until `min_seconds` have passed (at
-    most `max_steps`; each takes about 5 s of host work on the GPU machine).
+    most `max_steps`; each takes about 5 s of host work on an MI355X machine's CPU).
     Reported in TFLOP/s of the GEMM FLOPs per step."""
     import numpy as np
 
