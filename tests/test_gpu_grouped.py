@@ -116,7 +116,8 @@ def _check_grouped(c, qa, sa, qb, sb, offs, out, rows=None, bound=None):
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("counts,K,N", [([64, 0, 200, 17], 272, 256), ([1], 128, 128), ([300, 129], 144, 260),
                                         ([128] * 8, 512, 384), ([130, 0, 0, 1, 1000, 7, 256], 256, 1040),
-                                        ([200, 0, 77, 300], 1200, 384), ([129, 256], 2176, 256)])
+                                        ([200, 0, 77, 300], 1200, 384), ([129, 256], 2176, 256),
+                                        ([3, 130], 16, 256)])
 def test_grouped_small_within_bound(counts, K, N, out, accum):
     """Per-block-scaled N(0,1) activations and N(0,0.02) weights: the exact mode
     within the method's per-block bound, the FP8 matrix-core mode within the
@@ -125,6 +126,38 @@ def test_grouped_small_within_bound(counts, K, N, out, accum):
     c, qa, sa, qb, sb, offs = _grouped_case(counts, K, N, seed=len(counts) * 7 + K, out=out, accum=accum)
     bound = None if accum == "exact" else grouped_mfma8_bound(qa, sa, qb, sb, offs)
     _check_grouped(c, qa, sa, qb, sb, offs, out, bound=bound)
+
+
+@pytest.mark.parametrize("accum", ["exact", "mfma_fp8"])
+def test_grouped_offsets_not_monotone(accum):
+    """Offsets [20, 250, 100, 400, 380, 550] over 600 rows: each expert's interval
+    is clamped to [end of the previous one, total rows], giving [20, 250),
+    empty, [250, 400), empty, [400, 550); rows 0-19 and 550-599 belong to no
+    expert and keep what the output held.  The written rows are checked against
+    the oracle on the clamped offsets."""
+    dev = device()
+    rng = np.random.default_rng(24)
+    total, K, N = 600, 272, 256
+    raw = np.array([20, 250, 100, 400, 380, 550], dtype=np.int32)
+    eff = np.array([20, 250, 250, 400, 400, 550], dtype=np.int32)
+    G = raw.size - 1
+    announce(f"grouped non-monotone offsets {raw.tolist()} {accum}")
+    A32 = rng.standard_normal((total, K)).astype(np.float32)
+    B32 = (rng.standard_normal((G * N, K)) * 0.02).astype(np.float32)
+    qa, sa = gpu_blockwise(to_device((A32, "f32"), dev), 1)
+    qb, sb = gpu_blockwise(to_device((B32, "f32"), dev), 128)
+    c = torch.full((total, N), float("nan"), dtype=torch.float32, device=dev)
+    fm.fp8_grouped_gemm(qa, sa, qb.view(G, N, K), sb.view(G, N // 128, -1), torch.from_numpy(raw).to(dev), c,
+                        accum=accum)
+    torch.cuda.synchronize()
+    got = f32(c)
+    assert np.isnan(got[:20]).all() and np.isnan(got[550:]).all()
+    qa_h, sa_h = u8(qa), f32(sa)
+    qb_h = u8(qb).reshape(G, N, K)
+    sb_h = f32(sb).reshape(G, N // 128, -1)
+    rows = np.arange(20, 550)
+    bound = None if accum == "exact" else grouped_mfma8_bound(qa_h, sa_h, qb_h, sb_h, eff, rows=rows)
+    _check_grouped(got, qa_h, sa_h, qb_h, sb_h, eff, "f32", rows=rows, bound=bound)
 
 
 def test_grouped_equal_scales_reduce_to_dense_gemm():
