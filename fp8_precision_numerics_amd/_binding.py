@@ -347,7 +347,9 @@ def fp8_dequant_sum(q, fmt, scale_inv, out, stream=None) -> None:
         raise ValueError(f"out must have {n} elements")
     otype = F32 if out.dtype == torch.float32 else BF16
     with torch.cuda.device(dev):
-        _call("fp8_dequant_sum", lib.fp8_dequant_sum(_p(q), R, n, q.stride(0), _fmt(fmt), _p(scale_inv), _p(out),
+        # an empty payload addresses nothing: torch reports row stride 1 for [R x 0]
+        stride = q.stride(0) if n else 0
+        _call("fp8_dequant_sum", lib.fp8_dequant_sum(_p(q), R, n, stride, _fmt(fmt), _p(scale_inv), _p(out),
                                                      otype, _stream(stream)))
 
 
