@@ -29,6 +29,11 @@
 // * exact mode: the 16-deep bf16 instructions build P over eight sub-steps, so
 //   P and the accumulator are both live; 128x128 tiles of four 64x64 waves,
 //   two workgroups per CU.
+//
+// The A block scales (one per row and K step, rows far apart in memory) are
+// never loaded per lane and step: the exact mode stages them through LDS eight
+// steps at a time, the FP8 mode (whose LDS the slabs fill) has the four lanes
+// of a row share them through ds_bpermute.
 #include "gemm_kernel.hpp"
 #include "launch.hpp"
 
