@@ -52,9 +52,20 @@ def slab_accesses(BM, BN, NW, rows_left_a, rows_left_b, K, kt):
 SHAPES = [(256, 256, 4), (256, 256, 8), (128, 128, 4), (128, 512, 8)]
 
 
+# the largest K the entry points accept: dense 2^23 (256-row slabs; the
+# 128 x 128 tiles serve dense problems too), grouped 2^22 (the 128 x 512 tile's
+# 512-row B slab); the last row's offsets then come within 8 MiB of 2^31
+K_MAX_DENSE, K_MAX_GROUPED = 1 << 23, 1 << 22
+
+
+def _k_cases(BM, BN):
+    return [128, 400, 4096, K_MAX_GROUPED if (BM, BN) == (128, 512) else K_MAX_DENSE]
+
+
 @pytest.mark.parametrize("BM,BN,NW", SHAPES)
-@pytest.mark.parametrize("K", [128, 400, 4096])
-def test_slab_loads_stay_inside_the_operand(BM, BN, NW, K):
+@pytest.mark.parametrize("kcase", range(4))
+def test_slab_loads_stay_inside_the_operand(BM, BN, NW, kcase):
+    K = _k_cases(BM, BN)[kcase]
     nfull = K // KBK
     for rows_a, rows_b in [(1, BN), (BM, 1), (BM - 1, BN - 7), (9, 17), (BM // 2 + 3, BN // 2 - 5),
                            (BM, BN), (8 * NW - 1, 8 * NW + 1)]:
@@ -167,7 +178,8 @@ def bt_accesses(BN, NW, N, K, n0, kt, ragged):
 
 
 @pytest.mark.parametrize("BN,NW", [(256, 4), (256, 8), (128, 4)])
-@pytest.mark.parametrize("N,K", [(1040, 400), (256, 128), (16, 16), (528, 144), (2048, 4096)])
+@pytest.mark.parametrize("N,K", [(1040, 400), (256, 128), (16, 16), (528, 144), (2048, 4096),
+                                 (256, (1 << 23) - 128)])   # K * N at the entry point's 2^31 - 1 limit
 def test_bt_slab_loads_stay_inside_b_and_land_in_the_swizzled_layout(BN, NW, N, K):
     nrec = min(K * N, U32_MAX)
     nfull = K // KBK
@@ -319,3 +331,17 @@ def test_grouped_fp8_staggered_scale_groups_reach_every_step(nk):
                             assert got == (row, kt), (tile_rows, wm, kt, i, rr, got)
                 nxt = min(kt + 1, nk - 1)
                 sa_next = load(nxt & 3, nxt)
+
+
+def test_grouped_scale_offsets_at_the_largest_k():
+    """K = 2^22 (nk = 32768 steps): the largest VGPR offset either grouped kernel's
+    A-scale loads form (last row of the tile, last chunk or group, last lane)
+    stays a non-negative 32-bit value inside a full tile's resource."""
+    nk = K_MAX_GROUPED // KBK
+    # exact kernel: rows rb + (lane >> 3) < 128, steps chunk * 8 + (lane & 7)
+    last_chunk = (nk - 1) // 8
+    voff = ((63 >> 3) * nk + (63 & 7)) * 4 + (120 * nk + last_chunk * 8) * 4
+    assert voff + 4 <= 128 * nk * 4 < 2 ** 31
+    # FP8-core kernel: block 3, row 15 of the wave's 64 rows, step clamped to nk - 1
+    voff = ((3 * 16 + 15) * nk + (nk - 1)) * 4
+    assert voff + 4 <= 64 * nk * 4 < 2 ** 31
