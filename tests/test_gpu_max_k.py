@@ -1,5 +1,6 @@
 """GEMMs at the largest K each entry point accepts (include/fp8mi.h): dense
-2^23, dense with B stored [K x N] at K * N = 2^31 - 32768, grouped 2^22.
+2^23, dense with B stored [K x N] at K * N = 2^31 - 32768, grouped 2^22; and a
+cast of more than 2^31 elements.
 
 At these depths the slab loads' 32-bit buffer offsets come within a few MiB
 of 2^31 (the host replays in test_load_bounds.py check every one of them).
@@ -110,3 +111,37 @@ def test_grouped_gemm_at_the_largest_k(accum):
             s = sa_h[rows].astype(np.float64) @ sb_h[g, nb].astype(np.float64)       # sum over kb
             want[np.ix_(rows, cols)] = 128.0 * np.outer(a_vals[rows] * s, b_vals[g * N + cols])
     assert np.array_equal(got.view(np.uint32), want.astype(np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("transposed", [False, True])
+def test_cast_of_more_than_2_31_elements(transposed):
+    """bf16 131136 x 16384 (2^31 + 2^20 elements): zeros except four planted
+    values, one of them the very last element.  The flat cast (q only) and the
+    cast-transpose (q and q_t) must put each planted code at its place and
+    nothing else anywhere, and report the planted amax and saturation count."""
+    dev = device()
+    rows, cols = 131136, 16384
+    announce(f"cast of {rows}x{cols} bf16 (transposed={transposed})")
+    x = torch.zeros((rows, cols), dtype=torch.bfloat16, device=dev)
+    plant = {(rows - 1, cols - 1): 1000.0, (rows - 1, 0): -3.5, (rows // 2, 7): 0.1, (0, cols - 1): 2.0}
+    for (r, c), v in plant.items():
+        x[r, c] = v
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    q_t = torch.empty((cols, rows), dtype=torch.uint8, device=dev) if transposed else None
+    scale = torch.tensor([1.0], device=dev)
+    amax = torch.full((1,), 7.0, device=dev)
+    sat = torch.full((1,), 5, dtype=torch.int64, device=dev)
+    ws = torch.empty(fm.QUANTIZE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    fm.fp8_quantize(x, "e4m3", scale, q=q, q_t=q_t, amax=amax, sat=sat, workspace=ws)
+    torch.cuda.synchronize()
+    vals = np.array([float(x[r, c].float().item()) for (r, c) in plant], dtype=np.float32)   # as stored in bf16
+    want = codec.encode(vals, "e4m3")
+    for (r, c), code in zip(plant, want):
+        assert int(q[r, c].item()) == int(code), (r, c)
+        if transposed:
+            assert int(q_t[c, r].item()) == int(code), (r, c)
+    assert int(torch.count_nonzero(q).item()) == np.count_nonzero(want)
+    if transposed:
+        assert int(torch.count_nonzero(q_t).item()) == np.count_nonzero(want)
+    assert f32(amax).view(np.uint32)[0] == np.float32(np.abs(vals).max()).view(np.uint32)
+    assert int(sat.item()) == int(np.count_nonzero(np.abs(vals) > 448.0))
