@@ -1,7 +1,9 @@
-"""The delayed-scaling step (fused amax+cast, history update) captured in a HIP
-graph: every replay must match the same step run eagerly, with eager work and
-synchronisations between replays (graph memory nodes are not used by the
-path, and the cast's reduction goes through a workspace, not cleared memory)."""
+"""The path captured in HIP graphs: the delayed-scaling step (fused amax+cast,
+history update), the linear forward step, and the per-block / grouped and
+MXFP8 paths.  Every replay must match the same calls run eagerly, with eager
+work and synchronisations between replays (graph memory nodes are not used by
+the path, and the cast's reduction goes through a workspace, not cleared
+memory)."""
 
 import numpy as np
 import pytest
@@ -108,4 +110,65 @@ def test_graph_replays_match_eager_linear_forward_step():
         for k in ("qx", "qw"):
             assert torch.equal(g[k], e[k]), (replay, k)
         assert torch.equal(g["c"].view(torch.int16), e["c"].view(torch.int16)), replay
+        torch.zeros(1 << 20, device=dev).add_(1.0).sum().item()
+
+
+@pytest.mark.parametrize("accum", ["exact", "mfma_fp8"])
+def test_graph_replays_match_eager_blockwise_grouped_and_mx(accum):
+    """The per-block quantisers and the grouped GEMM (three experts, one empty),
+    the MXFP8 quantisers and the MXFP8 GEMM, captured in one graph: each of three
+    replays, with eager work between them, must give the codes, scales and
+    outputs of the same calls run eagerly, bit for bit."""
+    dev = device()
+    rng = np.random.default_rng(79)
+    G, N, K, total = 3, 256, 384, 256
+    offs = torch.tensor([0, 100, 100, total], dtype=torch.int32, device=dev)
+    A = torch.from_numpy(rng.standard_normal((total, K)).astype(np.float32)).to(dev).to(torch.bfloat16)
+    B = torch.from_numpy((rng.standard_normal((G * N, K)) * 0.02).astype(np.float32)).to(dev).to(torch.bfloat16)
+    X = torch.from_numpy(rng.standard_normal((256, 256)).astype(np.float32)).to(dev)
+    W = torch.from_numpy((rng.standard_normal((192, 256)) * 0.05).astype(np.float32)).to(dev)
+    nkb = (K + 127) // 128
+
+    def buffers():
+        u8 = dict(dtype=torch.uint8, device=dev)
+        return {"qa": torch.empty((total, K), **u8), "sa": torch.empty((total, nkb), device=dev),
+                "qb": torch.empty((G * N, K), **u8), "sb": torch.empty((G * N // 128, nkb), device=dev),
+                "c": torch.empty((total, N), device=dev),
+                "qx": torch.empty((256, 256), **u8), "sx": torch.empty(8 * fm.mx_scale_ld(256), **u8),
+                "qw": torch.empty((192, 256), **u8), "sw": torch.empty(8 * fm.mx_scale_ld(192), **u8),
+                "cm": torch.empty((256, 192), device=dev)}
+
+    def run(b):
+        fm.fp8_quantize_blockwise(A, 1, "e4m3", b["qa"], b["sa"])
+        fm.fp8_quantize_blockwise(B, 128, "e4m3", b["qb"], b["sb"])
+        fm.fp8_grouped_gemm(b["qa"], b["sa"], b["qb"].view(G, N, K), b["sb"].view(G, N // 128, nkb), offs, b["c"],
+                            accum=accum)
+        fm.fp8_quantize_mx(X, "e4m3", b["qx"], b["sx"])
+        fm.fp8_quantize_mx(W, "e4m3", b["qw"], b["sw"])
+        fm.fp8_gemm_mx(b["qx"], "e4m3", b["sx"], b["qw"], "e4m3", b["sw"], b["cm"], accum=accum)
+
+    g_buf, e_buf = buffers(), buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(g_buf)                                  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for t in g_buf.values():
+        t.zero_()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(g_buf)
+    for replay in range(3):
+        announce(f"graph replay {replay} blockwise/grouped/mx {accum}")
+        for t in e_buf.values():
+            t.zero_()
+        graph.replay()
+        run(e_buf)
+        torch.cuda.synchronize()
+        for k in g_buf:
+            a, b = g_buf[k], e_buf[k]
+            if a.dtype == torch.float32:
+                a, b = a.view(torch.int32), b.view(torch.int32)
+            assert torch.equal(a, b), (replay, k)
         torch.zeros(1 << 20, device=dev).add_(1.0).sum().item()
