@@ -1,6 +1,7 @@
 """The path captured in HIP graphs: the delayed-scaling step (fused amax+cast,
-history update), the linear forward step, and the per-block / grouped and
-MXFP8 paths.  Every replay must match the same calls run eagerly, with eager
+history update), the linear forward step, the per-block / grouped and MXFP8
+paths, the re-quantising GEMM and the all-reduce parts.  Every replay must
+match the same calls run eagerly, with eager
 work and synchronisations between replays (graph memory nodes are not used by
 the path, and the cast's reduction goes through a workspace, not cleared
 memory)."""
@@ -171,4 +172,57 @@ def test_graph_replays_match_eager_blockwise_grouped_and_mx(accum):
             if a.dtype == torch.float32:
                 a, b = a.view(torch.int32), b.view(torch.int32)
             assert torch.equal(a, b), (replay, k)
+        torch.zeros(1 << 20, device=dev).add_(1.0).sum().item()
+
+
+@pytest.mark.parametrize("accum", ["exact", "mfma_fp8"])
+def test_graph_replays_match_eager_requant_and_allreduce_parts(accum):
+    """The GEMM with its output re-quantised in the epilogue (which clears and
+    then accumulates its amax and count), and the all-reduce parts (shared scale
+    over eight ranks' amaxes, cast of each rank's gradient with it, sum of the
+    eight payloads), captured in one graph and replayed three times."""
+    dev = device()
+    rng = np.random.default_rng(80)
+    M, N, K, R, n = 320, 272, 256, 8, 4096
+    qa = torch.from_numpy(rng.integers(0, 0x7F, (M, K), dtype=np.uint8)).to(dev)
+    qb = torch.from_numpy(rng.integers(0, 0x7F, (N, K), dtype=np.uint8)).to(dev)
+    sa = torch.tensor([2.0 ** -9], device=dev)
+    sb = torch.tensor([2.0 ** -8], device=dev)
+    out_scale = torch.tensor([0.5], device=dev)
+    grads = torch.from_numpy((rng.standard_normal((R, n)) * 1e-3).astype(np.float32)).to(dev)
+    amaxes = grads.abs().amax(dim=1).contiguous()
+
+    def buffers():
+        return {"cq": torch.empty((M, N), dtype=torch.uint8, device=dev), "amax": torch.empty(1, device=dev),
+                "sat": torch.empty(1, dtype=torch.int64, device=dev), "scale": torch.empty(1, device=dev),
+                "scale_inv": torch.empty(1, device=dev), "q": torch.empty((R, n), dtype=torch.uint8, device=dev),
+                "sum": torch.empty(n, device=dev)}
+
+    def run(b):
+        fm.fp8_gemm_requant(qa, "e4m3", qb, "e4m3", sa, sb, "e4m3", out_scale, b["cq"], amax=b["amax"],
+                            sat=b["sat"], accum=accum)
+        fm.fp8_shared_scale(amaxes, "e5m2", b["scale"], b["scale_inv"])
+        for r in range(R):
+            fm.fp8_quantize(grads[r], "e5m2", b["scale"], q=b["q"][r])
+        fm.fp8_dequant_sum(b["q"], "e5m2", b["scale_inv"], b["sum"])
+
+    g_buf, e_buf = buffers(), buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(g_buf)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(g_buf)
+    for replay in range(3):
+        announce(f"graph replay {replay} requant/allreduce {accum}")
+        for t in list(g_buf.values()) + list(e_buf.values()):
+            t.view(torch.uint8).fill_(0xA5)              # junk that every call must overwrite
+        graph.replay()
+        run(e_buf)
+        torch.cuda.synchronize()
+        for k in g_buf:
+            assert torch.equal(g_buf[k].view(torch.uint8), e_buf[k].view(torch.uint8)), (replay, k)
         torch.zeros(1 << 20, device=dev).add_(1.0).sum().item()
