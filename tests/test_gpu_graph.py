@@ -1,10 +1,9 @@
 """The path captured in HIP graphs: the delayed-scaling step (fused amax+cast,
 history update), the linear forward step, the per-block / grouped and MXFP8
 paths, the re-quantising GEMM and the all-reduce parts.  Every replay must
-match the same calls run eagerly, with eager
-work and synchronisations between replays (graph memory nodes are not used by
-the path, and the cast's reduction goes through a workspace, not cleared
-memory)."""
+match the same calls run eagerly, with eager work and synchronisations between
+replays (graph memory nodes are not used by the path, and the cast's reduction
+goes through a workspace, not cleared memory)."""
 
 import numpy as np
 import pytest
